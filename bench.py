@@ -1,0 +1,188 @@
+"""Benchmark: paged GQA decode on Llama-3.1-8B shapes (one MI355X).
+
+One step = the whole decode hot path on one batch: write the step's new K/V
+into the paged cache (reshape_and_cache), then paged GQA attention with
+split-K partitions merged by log-sum-exp (paged_gqa_decode).  Workload: 64
+sequences, Hq=32, Hkv=8, d=128, block 16, bf16 cache, context U{512..4096},
+randomly permuted pages, seeded synthetic N(0,1) data.
+
+Metric: effective KV GB/s = sum(seq_len) * 2 * Hkv * d * 2 bytes / step time.
+Also reported: the decode kernel's roofline (HIP events on its launch
+stream), the mixed chunked-prefill + decode batch's tokens/s, and the CPU
+oracle's throughput on a bounded sample as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--mixed-partition", type=int, default=512)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def event_time_ms(fn, reps, stream):
+    """Average duration of fn() over reps calls, from HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(bt, seconds):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload.
+
+    The sample is whole passes over the batch's sequences (after the step's cache
+    write), repeated until `seconds` of CPU time have been spent.
+    """
+    from threadpoolctl import threadpool_limits
+    from oracle import cache_write_ref, decode_ref
+    kc, vc = cache_write_ref(bt.new_key, bt.new_value, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                             bt.query_start_loc)
+    per_tok = 2 * bt.num_kv_heads * bt.head_dim * bt.kv_itemsize
+    done_bytes, n_seq, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds:
+            for b in range(bt.num_seqs):
+                decode_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.num_kv_heads, bt.scale, seqs=[b])
+                done_bytes += int(bt.seq_lens[b]) * per_tok
+                n_seq += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seq} sequence decodes ({n_seq / bt.num_seqs:.2f} passes over the {bt.num_seqs}-sequence "
+                      f"batch), numpy fp64 with BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: multi-GPU runs are not part of this build "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    bt = wl.llama31_8b_decode(seed=args.seed)
+    up = lambda a: ops.to_device(a, dev)
+    q, kc, vc = up(bt.query), up(bt.key_cache), up(bt.value_cache)
+    nk, nv = up(bt.new_key), up(bt.new_value)
+    tables, lens, qsl = up(bt.block_tables), up(bt.seq_lens), up(bt.query_start_loc)
+    out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+    dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tables,
+                         q_dtype=q.dtype, out_dtype=out.dtype)
+    ws_bytes = ops.decode_workspace_size(dims, bt.max_seq_len, args.partition)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def decode():
+        ops.paged_gqa_decode(q, kc, vc, tables, lens, bt.max_seq_len, bt.scale, partition_size=args.partition,
+                             out=out, workspace=ws)
+
+    def step():
+        ops.reshape_and_cache(nk, nv, kc, vc, tables, lens, qsl)
+        decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    kv_bytes = bt.kv_bytes()
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the decode launch, timed with HIP events on its stream
+    decode_ms = event_time_ms(decode, max(20, args.steps // 2), stream)
+    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "paged_gqa_decode (decode + split-K merge)", "avg_ms": round(decode_ms, 5),
+                "bytes_per_launch": kv_bytes}
+
+    record = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": "llama31_8b_decode", "num_seqs": bt.num_seqs, "num_heads": bt.num_heads,
+                         "num_kv_heads": bt.num_kv_heads, "head_dim": bt.head_dim, "block_size": bt.block_size,
+                         "context": "U{512..4096}", "sum_seq_len": int(bt.seq_lens.sum()), "seed": args.seed,
+                         "partition_size": args.partition, "kv_dtype": "bf16", "out_dtype": "fp32",
+                         "step": "reshape_and_cache + paged_gqa_decode"},
+              "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+              "roofline": roofline}
+
+    if not args.no_mixed:
+        mb = wl.mixed_chunked(seed=4)
+        mq, mkc, mvc = up(mb.query), up(mb.key_cache), up(mb.value_cache)
+        mnk, mnv = up(mb.new_key), up(mb.new_value)
+        mt, ml, mqsl = up(mb.block_tables), up(mb.seq_lens), up(mb.query_start_loc)
+        mout = torch.empty(mb.num_tokens, mb.num_heads, mb.head_dim, dtype=torch.float32, device=dev)
+        mdims = ops.make_dims(num_seqs=mb.num_seqs, num_heads=mb.num_heads, key_cache=mkc, block_tables=mt,
+                              q_dtype=mq.dtype, out_dtype=mout.dtype)
+        mws = torch.zeros(max(ops.decode_workspace_size(mdims, mb.max_seq_len, args.mixed_partition), 1),
+                          dtype=torch.uint8, device=dev)
+        ops.reshape_and_cache(mnk, mnv, mkc, mvc, mt, ml, mqsl)
+
+        def mixed():
+            ops.chunked_prefill_paged_decode(mq, mkc, mvc, mt, ml, mqsl, mb.max_query_len, mb.max_seq_len, mb.scale,
+                                             partition_size=args.mixed_partition, out=mout, workspace=mws)
+        for _ in range(5):
+            mixed()
+        mixed_ms = event_time_ms(mixed, 50, stream)
+        ql = mb.query_lens.astype(np.int64)
+        prior = mb.seq_lens.astype(np.int64) - ql
+        flops = 4 * mb.head_dim * mb.num_heads * int(np.sum(ql * prior + ql * (ql + 1) // 2))
+        record["mixed_batch"] = {"workload": "mixed_chunked (256 seqs, 80% decode, lognormal chunks)",
+                                 "num_tokens": mb.num_tokens, "ms": round(mixed_ms, 5),
+                                 "tokens_per_s": round(mb.num_tokens / (mixed_ms * 1e-3), 1),
+                                 "algorithmic_gflop": round(flops / 1e9, 3),
+                                 "mfma_util": round(flops / (mixed_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+                                 "kv_gb": round(mb.kv_bytes() / 1e9, 4)}
+
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

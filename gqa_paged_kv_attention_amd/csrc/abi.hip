@@ -1,0 +1,257 @@
+// C ABI of libgqa_paged.so: host-side validation of scalar arguments, grid
+// sizing and kernel dispatch.  No allocation, no synchronisation, no state.
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/gqa_paged.h"
+#include "gqa_internal.h"
+
+namespace {
+
+constexpr int kTileTokens = 32;
+constexpr int kMaxGroup = 32;
+constexpr int kMaxSeqLen = 1 << 28;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_dims(const gqa_dims& d) {
+  if (d.num_seqs < 0 || d.num_heads <= 0 || d.num_kv_heads <= 0 || d.head_dim <= 0 || d.block_size <= 0 ||
+      d.num_blocks <= 0 || d.max_blocks_per_seq <= 0)
+    return GQA_ERR_INVALID_ARG;
+  if (d.num_heads % d.num_kv_heads != 0) return GQA_ERR_INVALID_ARG;
+  if (d.q_dtype != GQA_F32 && d.q_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (d.kv_dtype != GQA_F32 && d.kv_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (d.out_dtype != GQA_F32 && d.out_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (d.head_dim != 64 && d.head_dim != 128) return GQA_ERR_UNSUPPORTED;
+  if (d.block_size != 16) return GQA_ERR_UNSUPPORTED;
+  if (d.q_dtype != d.kv_dtype) return GQA_ERR_UNSUPPORTED;
+  if ((long long)d.max_blocks_per_seq * d.block_size > kMaxSeqLen) return GQA_ERR_UNSUPPORTED;
+  if (d.num_seqs > 65535) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+// Effective partitioning: tokens per partition and number of partitions.
+bool partitioning(int32_t max_seq_len, int32_t partition_size, int* psize, int* nparts) {
+  if (max_seq_len < 0 || max_seq_len > kMaxSeqLen || partition_size < 0) return false;
+  if (partition_size > 0 && partition_size % kTileTokens != 0) return false;
+  if (partition_size == 0 || partition_size >= max_seq_len) {
+    const int p = max_seq_len <= 0 ? kTileTokens : (max_seq_len + kTileTokens - 1) / kTileTokens * kTileTokens;
+    *psize = partition_size > 0 ? (p > partition_size ? p : partition_size) : p;
+    *nparts = 1;
+  } else {
+    *psize = partition_size;
+    *nparts = (max_seq_len + partition_size - 1) / partition_size;
+  }
+  return true;
+}
+
+size_t partial_bytes(const gqa_dims& d, int nparts) {
+  if (nparts <= 1) return 0;
+  const size_t rows = (size_t)d.num_seqs * d.num_heads * nparts;
+  return align_up(rows * d.head_dim * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+int status_from(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH; }
+
+// Decode launch shared by paged_gqa_decode and the decode half of the mixed call.
+int run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+               const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
+               int32_t num_tokens, int32_t max_seq_len, const gqa_dims& dims, float scale, int32_t partition_size,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int psize = 0, nparts = 0;
+  if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
+  const size_t need = partial_bytes(dims, nparts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+  if (dims.num_seqs == 0) return GQA_OK;
+
+  gqa::DecodeArgs a;
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  const size_t rows = (size_t)dims.num_seqs * dims.num_heads * nparts;
+  a.partial_out = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.partial_lse = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                                   align_up(rows * dims.head_dim * sizeof(float)))
+                       : nullptr;
+  a.num_heads = dims.num_heads;
+  a.num_kv_heads = dims.num_kv_heads;
+  a.group = dims.num_heads / dims.num_kv_heads;
+  a.num_blocks = dims.num_blocks;
+  a.max_blocks_per_seq = dims.max_blocks_per_seq;
+  a.num_tokens = num_tokens;
+  a.partition_size = psize;
+  a.max_partitions = nparts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
+  hipError_t e = gqa::launch_decode(a, dims.head_dim, kv_f32, out_f32, dims.num_seqs, stream);
+  if (e != hipSuccess) return GQA_ERR_LAUNCH;
+  if (nparts > 1) {
+    gqa::ReduceArgs r;
+    r.out = out;
+    r.partial_out = a.partial_out;
+    r.partial_lse = a.partial_lse;
+    r.seq_lens = seq_lens;
+    r.query_start_loc = query_start_loc;
+    r.num_heads = dims.num_heads;
+    r.max_blocks_per_seq = dims.max_blocks_per_seq;
+    r.max_partitions = nparts;
+    r.partition_size = psize;
+    r.num_tokens = num_tokens;
+    r.skip_single = 1;
+    e = gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, stream);
+  }
+  return status_from(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int32_t status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t gqa_version(void) { return 100; }
+
+int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
+                          int32_t num_tokens, gqa_dims dims, void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (num_tokens < 0) return GQA_ERR_INVALID_ARG;
+  if (num_tokens == 0 || dims.num_seqs == 0) return GQA_OK;
+  if (!key || !value || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc)
+    return GQA_ERR_INVALID_ARG;
+  gqa::CacheWriteArgs a;
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = dims.num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = dims.num_kv_heads;
+  a.num_blocks = dims.num_blocks;
+  a.max_blocks_per_seq = dims.max_blocks_per_seq;
+  return status_from(gqa::launch_cache_write(a, dims.head_dim, dims.kv_dtype == GQA_F32,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t paged_gqa_decode_workspace_size(gqa_dims dims, int32_t max_seq_len, int32_t partition_size) {
+  int psize = 0, nparts = 0;
+  if (check_dims(dims) != GQA_OK || !partitioning(max_seq_len, partition_size, &psize, &nparts)) return 0;
+  return partial_bytes(dims, nparts);
+}
+
+int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int32_t max_seq_len, gqa_dims dims,
+                         float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens))
+    return GQA_ERR_INVALID_ARG;
+  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
+                    max_seq_len, dims, scale, partition_size, workspace, workspace_bytes,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* partial_lse, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, gqa_dims dims, int32_t max_partitions,
+                          int32_t partition_size, int32_t skip_single, void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (max_partitions <= 0 || partition_size <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs == 0) return GQA_OK;
+  if (!out || !partial_out || !partial_lse || !seq_lens) return GQA_ERR_INVALID_ARG;
+  gqa::ReduceArgs r;
+  r.out = out;
+  r.partial_out = partial_out;
+  r.partial_lse = partial_lse;
+  r.seq_lens = seq_lens;
+  r.query_start_loc = query_start_loc;
+  r.num_heads = dims.num_heads;
+  r.max_blocks_per_seq = dims.max_blocks_per_seq;
+  r.max_partitions = max_partitions;
+  r.partition_size = partition_size;
+  r.num_tokens = query_start_loc ? 0x7fffffff : dims.num_seqs;
+  r.skip_single = skip_single;
+  return status_from(gqa::launch_reduce(r, dims.head_dim, dims.out_dtype == GQA_F32, dims.num_seqs,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t chunked_prefill_paged_decode_workspace_size(gqa_dims dims, int32_t max_seq_len, int32_t partition_size) {
+  return paged_gqa_decode_workspace_size(dims, max_seq_len, partition_size);
+}
+
+int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                                     int32_t max_seq_len, gqa_dims dims, float scale, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || num_tokens < 0 || max_query_len < 0) return GQA_ERR_INVALID_ARG;
+  if (max_query_len > max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs == 0 || num_tokens == 0) {
+    int ps = 0, np = 0;
+    return partitioning(max_seq_len, partition_size, &ps, &np) ? GQA_OK : GQA_ERR_INVALID_ARG;
+  }
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc)
+    return GQA_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    int ps = 0, np = 0;
+    if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
+    const size_t need = partial_bytes(dims, np);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+  }
+  if (max_query_len > 1) {
+    gqa::PrefillArgs p;
+    p.out = out;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.query_start_loc = query_start_loc;
+    p.num_seqs = dims.num_seqs;
+    p.num_heads = dims.num_heads;
+    p.num_kv_heads = dims.num_kv_heads;
+    p.group = dims.num_heads / dims.num_kv_heads;
+    p.num_blocks = dims.num_blocks;
+    p.max_blocks_per_seq = dims.max_blocks_per_seq;
+    p.num_tokens = num_tokens;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    const long long rpg = gqa::prefill_rows_per_group();
+    // Upper bound on row tiles: every prefill sequence wastes at most one partial tile.
+    const long long prefill_seqs = std::min<long long>(dims.num_seqs, num_tokens / 2);
+    const long long tiles = ((long long)num_tokens * p.group + rpg - 1) / rpg + prefill_seqs;
+    const long long groups = tiles * dims.num_kv_heads;
+    if (groups > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    hipError_t e = gqa::launch_prefill(p, dims.head_dim, dims.kv_dtype == GQA_F32, dims.out_dtype == GQA_F32,
+                                       (int)groups, s);
+    if (e != hipSuccess) return GQA_ERR_LAUNCH;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
+                    max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,308 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core formulation.  For a tile of key tokens and a block of 16 query
+// rows (a GQA group's heads, or (token, head) pairs of a prefill chunk):
+//
+//   S^T[t][r] = sum_d K[t][d] * Q[r][d]          A = K tile,  B = Q^T
+//   O^T[d][r] += sum_t V^T[d][t] * P^T[t][r]     A = V^T tile, B = P^T
+//
+// With the key page stored token-major ([bs][d]) and the value page stored
+// channel-major ([d][bs]), every A operand is a contiguous 16-byte load per
+// lane, and the score fragment that the first product leaves in a lane is
+// exactly the P^T fragment the second product needs from that lane, so the
+// softmax runs in registers with no LDS round trip.
+//
+// Operand layouts of the 16x16 MFMAs used here (wave64, lane l, n = l % 16,
+// q = l / 16):
+//   A[m][k]: lane l holds row m = n and a run of k indices owned by group q
+//   B[k][c]: lane l holds column c = n and the same run of k indices
+//   D[m][c]: lane l holds column c = n, rows m = 4q + j (j = 0..3)
+// Because the contraction index k only has to agree between A and B, the
+// kernels are free to choose which memory element feeds which k slot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 32;        // key tokens per tile (two 16-token pages)
+constexpr int kPage = 16;        // block_size
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// bf16 (as 16-bit pattern) from float, round to nearest even (hardware convert).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max across the four lane groups that share a row (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float row_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Page id through the block table, clamped into the pool so that a corrupt
+// entry can give a wrong answer but never an out-of-bounds read.
+__device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_blocks) {
+  int p = bt_row[idx];
+  return (unsigned)p < (unsigned)num_blocks ? p : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Tile operations, specialised by cache dtype.  A "tile" is 32 key tokens of
+// one kv head spread over two pages (A = tokens 0..15, B = tokens 16..31).
+// Each lane ends a Q.K^T product holding 8 scores per 16-row block, indexed
+// idx = 0..7; token_offset(q, idx) gives their key offsets inside the tile.
+// ---------------------------------------------------------------------------
+
+// bf16 caches: v_mfma_f32_16x16x32_bf16.
+//  - Q.K^T: two products per 16-row block, each over 16 tokens.  Product s
+//    feeds row m of A with token (m < 8 ? page A : page B), slot
+//    (m & 3) + 8 * ((m >> 2) & 1) + 4 * s, and k slots 8q..8q+7 of chunk kk with
+//    channels 32 kk + 8q .. +7.  Lane group q then holds tokens 8q + idx.
+//  - P.V: one product per 16 channels over the whole 32-token tile; lane group
+//    q supplies k slots 8q..8q+7 = tokens 8q .. 8q+7 (page q >= 2 ? B : A,
+//    slots 8 (q & 1) ..), a contiguous 16-byte run of the channel-major page.
+//  - P is fed as a hi/lo pair of bf16 (p = hi + lo to ~2^-16 relative), so the
+//    P.V product keeps fp32-grade weights.
+template <int D>
+struct TileBF16 {
+  static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
+  static constexpr int DT = D / 16;   // 16-channel blocks of the output
+  struct K { uint4 v[2][KC]; };
+  struct V { uint4 v[DT]; };
+  struct Q { uint4 v[KC]; };
+  typedef uint16_t elem_t;
+
+  __device__ __forceinline__ static int token_offset(int q, int idx) { return 8 * q + idx; }
+  __device__ __forceinline__ static int v_token_offset(int q, int e) { return 8 * q + e; }
+
+  // kA/kB: key page base for this kv head ([bs][D] elements).
+  __device__ __forceinline__ static void load_k(K& k, const elem_t* kA, const elem_t* kB, int lane) {
+    const int m = lane & 15, q = lane >> 4;
+    const elem_t* pg = (m < 8) ? kA : kB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int slot = (m & 3) + 8 * ((m >> 2) & 1) + 4 * s;
+      const elem_t* row = pg + slot * D + 8 * q;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) k.v[s][c] = ld16(row + 32 * c);
+    }
+  }
+
+  // vA/vB: value page base for this kv head ([D][bs] elements).
+  __device__ __forceinline__ static void load_v(V& v, const elem_t* vA, const elem_t* vB, int lane) {
+    const int n = lane & 15, q = lane >> 4;
+    const elem_t* pg = (q < 2) ? vA : vB;
+    const elem_t* base = pg + n * kPage + 8 * (q & 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v.v[dt] = ld16(base + dt * 16 * kPage);
+  }
+
+  // row: query row base ([D] elements) or nullptr for a padding row.
+  __device__ __forceinline__ static void load_q(Q& qf, const elem_t* row, int lane) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf.v[c] = row ? ld16(row + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+  }
+
+  __device__ __forceinline__ static void qk(float s[8], const K& k, const Q& qf) {
+    f32x4_t acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      acc0 = mfma_bf16(k.v[0][c], qf.v[c], acc0);
+      acc1 = mfma_bf16(k.v[1][c], qf.v[c], acc1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { s[j] = acc0[j]; s[4 + j] = acc1[j]; }
+  }
+
+  // Zero value elements of tokens at or past `end` (offsets relative to the tile).
+  __device__ __forceinline__ static void mask_v(V& v, int tile_base, int end, int lane) {
+    const int q = lane >> 4;
+    const int first = tile_base + 8 * q;
+    uint32_t keep[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (first + 2 * w) < end ? 0xFFFFu : 0u;
+      const uint32_t hi = (first + 2 * w + 1) < end ? 0xFFFF0000u : 0u;
+      keep[w] = lo | hi;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      v.v[dt].x &= keep[0];
+      v.v[dt].y &= keep[1];
+      v.v[dt].z &= keep[2];
+      v.v[dt].w &= keep[3];
+    }
+  }
+
+  __device__ __forceinline__ static void pv(f32x4_t o[DT], const V& v, const float p[8]) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint16_t h0 = float_to_bf16_bits(p[2 * w]);
+      const uint16_t h1 = float_to_bf16_bits(p[2 * w + 1]);
+      const uint16_t l0 = float_to_bf16_bits(p[2 * w] - bf16_bits_to_float(h0));
+      const uint16_t l1 = float_to_bf16_bits(p[2 * w + 1] - bf16_bits_to_float(h1));
+      hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lo[w] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = mfma_bf16(v.v[dt], phi, o[dt]);
+      o[dt] = mfma_bf16(v.v[dt], plo, o[dt]);
+    }
+  }
+};
+
+// fp32 caches: v_mfma_f32_16x16x4_f32 (exact fp32 products).
+//  - Q.K^T: per page s, A row m = slot m; a 16-byte load gives channels
+//    16c + 4q .. +3, consumed by four products (k slot q <-> channel 16c+4q+i).
+//    Lane group q then holds tokens 16 s + 4q + j.
+//  - P.V: per page s and channel block, a 16-byte load of the channel-major
+//    page gives slots 4q .. 4q+3, consumed by four products (k slot q <-> slot
+//    4q + i), whose B operand is the lane's own score for that token.
+template <int D>
+struct TileF32 {
+  static constexpr int KC = D / 16;
+  static constexpr int DT = D / 16;
+  struct K { float4 v[2][KC]; };
+  struct V { float4 v[2][DT]; };
+  struct Q { float4 v[KC]; };
+  typedef float elem_t;
+
+  __device__ __forceinline__ static int token_offset(int q, int idx) {
+    return 16 * (idx >> 2) + 4 * q + (idx & 3);
+  }
+
+  __device__ __forceinline__ static void load_k(K& k, const elem_t* kA, const elem_t* kB, int lane) {
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const elem_t* row = (s ? kB : kA) + m * D + 4 * q;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) k.v[s][c] = *reinterpret_cast<const float4*>(row + 16 * c);
+    }
+  }
+
+  __device__ __forceinline__ static void load_v(V& v, const elem_t* vA, const elem_t* vB, int lane) {
+    const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const elem_t* base = (s ? vB : vA) + n * kPage + 4 * q;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) v.v[s][dt] = *reinterpret_cast<const float4*>(base + dt * 16 * kPage);
+    }
+  }
+
+  __device__ __forceinline__ static void load_q(Q& qf, const elem_t* row, int lane) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qf.v[c] = row ? *reinterpret_cast<const float4*>(row + 16 * c + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  __device__ __forceinline__ static void qk(float s[8], const K& k, const Q& qf) {
+    f32x4_t acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      acc0 = mfma_f32(k.v[0][c].x, qf.v[c].x, acc0);
+      acc0 = mfma_f32(k.v[0][c].y, qf.v[c].y, acc0);
+      acc0 = mfma_f32(k.v[0][c].z, qf.v[c].z, acc0);
+      acc0 = mfma_f32(k.v[0][c].w, qf.v[c].w, acc0);
+      acc1 = mfma_f32(k.v[1][c].x, qf.v[c].x, acc1);
+      acc1 = mfma_f32(k.v[1][c].y, qf.v[c].y, acc1);
+      acc1 = mfma_f32(k.v[1][c].z, qf.v[c].z, acc1);
+      acc1 = mfma_f32(k.v[1][c].w, qf.v[c].w, acc1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { s[j] = acc0[j]; s[4 + j] = acc1[j]; }
+  }
+
+  __device__ __forceinline__ static void mask_v(V& v, int tile_base, int end, int lane) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int first = tile_base + 16 * s + 4 * q;
+      const bool k0 = first < end, k1 = first + 1 < end, k2 = first + 2 < end, k3 = first + 3 < end;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        float4& x = v.v[s][dt];
+        x.x = k0 ? x.x : 0.f;
+        x.y = k1 ? x.y : 0.f;
+        x.z = k2 ? x.z : 0.f;
+        x.w = k3 ? x.w : 0.f;
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void pv(f32x4_t o[DT], const V& v, const float p[8]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        o[dt] = mfma_f32(v.v[s][dt].x, p[4 * s + 0], o[dt]);
+        o[dt] = mfma_f32(v.v[s][dt].y, p[4 * s + 1], o[dt]);
+        o[dt] = mfma_f32(v.v[s][dt].z, p[4 * s + 2], o[dt]);
+        o[dt] = mfma_f32(v.v[s][dt].w, p[4 * s + 3], o[dt]);
+      }
+    }
+  }
+};
+
+// Store 4 consecutive output channels (fp32 values) as fp32 or bf16.
+__device__ __forceinline__ void store4(float* dst, f32x4_t x) {
+  *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4(uint16_t* dst, f32x4_t x) {
+  const uint32_t a = (uint32_t)float_to_bf16_bits(x[0]) | ((uint32_t)float_to_bf16_bits(x[1]) << 16);
+  const uint32_t b = (uint32_t)float_to_bf16_bits(x[2]) | ((uint32_t)float_to_bf16_bits(x[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(a, b);
+}
+__device__ __forceinline__ void store1(float* dst, float x) { *dst = x; }
+__device__ __forceinline__ void store1(uint16_t* dst, float x) { *dst = float_to_bf16_bits(x); }
+
+}  // namespace gqa

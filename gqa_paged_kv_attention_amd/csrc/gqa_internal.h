@@ -1,0 +1,87 @@
+// Host-side launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;   // nullptr: query row = sequence index
+  float* partial_out;               // [B, Hq, max_partitions, D]
+  float* partial_lse;               // [B, Hq, max_partitions]
+  int num_heads;
+  int num_kv_heads;
+  int group;                        // num_heads / num_kv_heads
+  int num_blocks;
+  int max_blocks_per_seq;
+  int num_tokens;
+  int partition_size;               // tokens per partition, multiple of 32
+  int max_partitions;
+  float scale_log2;                 // scale * log2(e)
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int num_tokens;
+  float scale_log2;
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* partial_out;
+  const float* partial_lse;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  int num_heads;
+  int max_blocks_per_seq;
+  int max_partitions;
+  int partition_size;
+  int num_tokens;
+  int skip_single;
+};
+
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  int num_seqs;
+  int num_tokens;
+  int num_kv_heads;
+  int num_blocks;
+  int max_blocks_per_seq;
+};
+
+// kv_f32 / out_f32 select fp32 (true) or bf16 (false) storage.
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool kv_f32, bool out_f32, int num_seqs,
+                         hipStream_t stream);
+// Rows per prefill work-group (depends only on the build).
+int prefill_rows_per_group();
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,
+                          hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,75 @@
+// reshape_and_cache: write this step's keys/values into the paged caches.
+//
+// Incoming key/value rows are [tokens, num_kv_heads, head_dim] ("[Performance]
+// Use optimized kernels for MQA/GQA", opening post, item 1).  New token j of
+// sequence b is the sequence's position seq_lens[b] - q_len + j; it lands in
+// page block_tables[b][pos / bs] at slot pos % bs.  Keys go to the token-major
+// key page ([bs][d]); values to the channel-major value page ([d][bs]).  The
+// copy moves bit patterns, so it is exact for any storage dtype.
+#include "gqa_common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread per (token, kv head, 16-byte chunk of the head): VEC elements.
+template <int D, class T>
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CH = D / VEC;
+  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long per_tok = (long long)a.num_kv_heads * CH;
+  if (gid >= (long long)a.num_tokens * per_tok) return;
+  const int tok = (int)(gid / per_tok);
+  const int rem = (int)(gid % per_tok);
+  const int kv = rem / CH, c = rem % CH;
+
+  // sequence owning this token: last b with query_start_loc[b] <= tok
+  int lo = 0, hi = a.num_seqs;           // invariant: qsl[lo] <= tok < qsl[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.query_start_loc[mid] <= tok) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+  if (tok < q0 || tok >= q1) return;
+  const int pos = a.seq_lens[b] - (q1 - q0) + (tok - q0);
+  if (pos < 0 || pos >= a.max_blocks_per_seq * kPage) return;
+  const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kPage];
+  if ((unsigned)page >= (unsigned)a.num_blocks) return;
+  const int slot = pos % kPage;
+
+  const size_t src = ((size_t)tok * a.num_kv_heads + kv) * D + c * VEC;
+  const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)(kPage * D);
+  const uint4 kx = ld16(reinterpret_cast<const T*>(a.key) + src);
+  *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.key_cache) + pbase + (size_t)slot * D + c * VEC) = kx;
+
+  const uint4 vx = ld16(reinterpret_cast<const T*>(a.value) + src);
+  T vals[VEC];
+  __builtin_memcpy(vals, &vx, 16);
+  T* vdst = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)(c * VEC) * kPage + slot;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) vdst[(size_t)e * kPage] = vals[e];
+}
+
+template <class T>
+hipError_t dispatch(const CacheWriteArgs& a, int D, hipStream_t s) {
+  const long long total = (long long)a.num_tokens * a.num_kv_heads * (D * (long long)sizeof(T) / 16);
+  const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
+  if (D == 64)
+    hipLaunchKernelGGL((cache_write_kernel<64, T>), dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((cache_write_kernel<128, T>), dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream) {
+  return kv_f32 ? dispatch<float>(a, head_dim, stream) : dispatch<uint16_t>(a, head_dim, stream);
+}
+
+}  // namespace gqa

@@ -1,0 +1,245 @@
+"""ctypes binding over libgqa_paged.so (the C ABI in include/gqa_paged.h).
+
+Argument marshalling only: shapes are read off torch tensors, device pointers
+and the current HIP stream are handed to the library, and a nonzero status
+raises.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  Torch provides device memory (outputs and workspaces)
+and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_paged.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gqa_paged.h")
+
+GQA_F32, GQA_BF16 = 0, 1
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
+          4: "GQA_ERR_LAUNCH"}
+
+
+class GqaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqa_paged.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gqa_paged_kv_attention_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [i32], ctypes.c_char_p
+    lib.gqa_version.argtypes, lib.gqa_version.restype = [], i32
+    lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, Dims, vp]
+    lib.reshape_and_cache.restype = i32
+    lib.paged_gqa_decode_workspace_size.argtypes = [Dims, i32, i32]
+    lib.paged_gqa_decode_workspace_size.restype = sz
+    lib.paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
+    lib.paged_gqa_decode.restype = i32
+    lib.splitk_lse_reduce.argtypes = [vp, vp, vp, vp, vp, Dims, i32, i32, i32, vp]
+    lib.splitk_lse_reduce.restype = i32
+    lib.chunked_prefill_paged_decode_workspace_size.argtypes = [Dims, i32, i32]
+    lib.chunked_prefill_paged_decode_workspace_size.restype = sz
+    lib.chunked_prefill_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, Dims, f32, i32, vp, sz,
+                                                 vp]
+    lib.chunked_prefill_paged_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER_PATH):
+    """Names of the functions include/gqa_paged.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GQA_F32
+    if t == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.float32 if code == GQA_F32 else torch.bfloat16
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _check_int32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("block_tables, seq_lens and query_start_loc must be int32")
+
+
+def make_dims(*, num_seqs, num_heads, key_cache, block_tables, q_dtype, out_dtype) -> Dims:
+    nb, hkv, bs, d = key_cache.shape
+    return Dims(num_seqs, num_heads, hkv, d, bs, nb, block_tables.shape[1], _dtype_code(q_dtype),
+                _dtype_code(key_cache.dtype), _dtype_code(out_dtype))
+
+
+def _call(fn: str, status: int):
+    if status != 0:
+        lib = load_library()
+        raise GqaError(fn, status, lib.gqa_status_string(status).decode())
+
+
+# --------------------------------------------------------------------------
+# public API (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def reshape_and_cache(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc, stream=None):
+    """Write new keys/values ``[T, Hkv, d]`` into the paged caches (in place)."""
+    lib = load_library()
+    _check_device(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc)
+    _check_int32(block_tables, seq_lens, query_start_loc)
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise TypeError("key/value and caches must share a dtype")
+    dims = make_dims(num_seqs=seq_lens.shape[0], num_heads=key_cache.shape[1], key_cache=key_cache,
+                     block_tables=block_tables, q_dtype=key.dtype, out_dtype=key.dtype)
+    _call("reshape_and_cache", lib.reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                                     _ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc),
+                                                     key.shape[0], dims, _stream(stream)))
+
+
+def decode_workspace_size(dims: Dims, max_seq_len: int, partition_size: int) -> int:
+    return int(load_library().paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace too small: need {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+                     partition_size: int = 0, out=None, out_dtype=None, workspace=None, stream=None):
+    """Decode attention: ``query [B, Hq, d]`` -> ``out [B, Hq, d]``."""
+    lib = load_library()
+    _check_device(query, key_cache, value_cache, block_tables, seq_lens, out, workspace)
+    _check_int32(block_tables, seq_lens)
+    B, Hq, d = query.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=B, num_heads=Hq, key_cache=key_cache, block_tables=block_tables, q_dtype=query.dtype,
+                     out_dtype=out_dtype)
+    nbytes = int(lib.paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
+    _call("paged_gqa_decode", lib.paged_gqa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                                   _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
+                                                   float(scale), int(partition_size), _ptr(ws), wsb,
+                                                   _stream(stream)))
+    return out
+
+
+def splitk_lse_reduce(partial_out, partial_lse, seq_lens, partition_size: int, *, num_kv_heads: int,
+                      block_size: int = 16, max_blocks_per_seq: int, query_start_loc=None, out=None,
+                      out_dtype=None, skip_single: bool = False, num_out_rows: Optional[int] = None, stream=None):
+    """Merge split-K partials ``[B, Hq, P, d]`` / ``[B, Hq, P]`` into ``out``."""
+    lib = load_library()
+    _check_device(partial_out, partial_lse, seq_lens, query_start_loc, out)
+    _check_int32(seq_lens, query_start_loc)
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    B, Hq, P, d = partial_out.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        rows = num_out_rows if num_out_rows is not None else B
+        out = torch.zeros(rows, Hq, d, dtype=out_dtype, device=partial_out.device)
+    dims = Dims(B, Hq, num_kv_heads, d, block_size, 1, max_blocks_per_seq, _dtype_code(out_dtype),
+                _dtype_code(out_dtype), _dtype_code(out_dtype))
+    _call("splitk_lse_reduce", lib.splitk_lse_reduce(_ptr(out), _ptr(partial_out), _ptr(partial_lse), _ptr(seq_lens),
+                                                     _ptr(query_start_loc), dims, P, int(partition_size),
+                                                     int(bool(skip_single)), _stream(stream)))
+    return out
+
+
+def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
+                                 max_query_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
+                                 out=None, out_dtype=None, workspace=None, stream=None):
+    """Mixed prefill-chunk + decode attention: ``query [T, Hq, d]`` -> ``out [T, Hq, d]``."""
+    lib = load_library()
+    _check_device(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, out, workspace)
+    _check_int32(block_tables, seq_lens, query_start_loc)
+    T, Hq, d = query.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(T, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=seq_lens.shape[0], num_heads=Hq, key_cache=key_cache, block_tables=block_tables,
+                     q_dtype=query.dtype, out_dtype=out_dtype)
+    nbytes = int(lib.chunked_prefill_paged_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
+    _call("chunked_prefill_paged_decode",
+          lib.chunked_prefill_paged_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                           _ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc), T,
+                                           int(max_query_len), int(max_seq_len), dims, float(scale),
+                                           int(partition_size), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def to_device(arr, device="cuda") -> torch.Tensor:
+    """Host storage array -> device tensor (uint16 bit patterns become bfloat16)."""
+    import numpy as np
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(arr).to(device)
+
+
+def to_host_storage(t: torch.Tensor):
+    """Device tensor -> host storage array (bfloat16 becomes uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()

@@ -29,8 +29,10 @@ which a lognormal length mix stands in.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -39,16 +41,42 @@ BF16 = "bf16"
 F32 = "f32"
 
 
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(n: int, fn) -> None:
+    """Run fn(start, stop) over [0, n) in fixed-size chunks on a thread pool."""
+    starts = range(0, n, _CHUNK)
+    if len(starts) <= 1:
+        for s in starts:
+            fn(s, min(n, s + _CHUNK))
+        return
+    with cf.ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(lambda s: fn(s, min(n, s + _CHUNK)), starts))
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest-even bfloat16; return uint16 bits."""
+    """Round float32 values to the nearest-even bfloat16; return uint16 bits.
+
+    NaNs map to the quiet NaN 0x7FC0; the uint32 sum below can only wrap for
+    NaN bit patterns, which are overwritten.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        out[nan] = 0x7FC0
-    return out
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+
+    def conv(a, b):
+        u = flat[a:b].view(np.uint32)
+        r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        o = r.astype(np.uint16)
+        nan = np.isnan(flat[a:b])
+        if nan.any():
+            o[nan] = 0x7FC0
+        out[a:b] = o
+
+    _chunked(flat.size, conv)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -62,7 +90,20 @@ def storage_to_f32(arr: np.ndarray) -> np.ndarray:
 
 
 def _normal_storage(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    vals = rng.standard_normal(size=shape, dtype=np.float32)
+    """N(0,1) float32 values in storage form.
+
+    Each 4M-element chunk draws from its own PCG64 stream spawned from one seed
+    taken from ``rng``, so the values do not depend on the thread count.
+    """
+    n = int(np.prod(shape))
+    vals = np.empty(n, dtype=np.float32)
+    kids = np.random.SeedSequence(int(rng.integers(0, 2 ** 63))).spawn(max(1, -(-n // _CHUNK)))
+
+    def fill(a, b):
+        np.random.Generator(np.random.PCG64(kids[a // _CHUNK])).standard_normal(out=vals[a:b], dtype=np.float32)
+
+    _chunked(n, fill)
+    vals = vals.reshape(shape)
     if dtype == BF16:
         return f32_to_bf16_bits(vals)
     if dtype == F32:

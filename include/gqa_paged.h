@@ -1,0 +1,174 @@
+/*
+ * gqa_paged.h - GQA/MQA-aware attention over a paged KV cache, MI355X (gfx950).
+ *
+ * C ABI of libgqa_paged.so.  Every pointer argument named *_cache, query, key,
+ * value, out, block_tables, seq_lens, query_start_loc, partial_* and workspace
+ * is a DEVICE pointer owned by the caller; `stream` is a hipStream_t cast to
+ * void* (NULL = the null stream).  Calls only enqueue work on `stream` and
+ * return without synchronising; the library allocates nothing, frees nothing
+ * and keeps no state between calls (it is re-entrant; two calls that share a
+ * workspace must not overlap).
+ *
+ * The operation follows three pages:
+ *  - "[Performance] Use optimized kernels for MQA/GQA" (vLLM issue #1880),
+ *    opening post: several query heads share one kv head, and attention should
+ *    read the KV cache once per kv head instead of expanding K/V per query head
+ *    (item 1, the expand of keys/values with a group axis after the kv-head
+ *    axis); the decode reads a paged KV cache (item 2).
+ *  - "[Kernel] [V1] Further optimizations to ROCm (Triton) Backend to better
+ *    handle GQA" (vLLM PR #14431), TLDR and review thread: one op,
+ *    chunked_prefill_paged_decode, serves a batch that mixes prefill chunks and
+ *    single-token decodes over the same paged cache; the prefill part skips the
+ *    decodes and a second kernel handles them.
+ *
+ * Semantics, for sequence b, query head h, G = num_heads / num_kv_heads:
+ *   kv   = h / G                              (heads of a group are contiguous)
+ *   q_len = query_start_loc[b+1] - query_start_loc[b]   (decode: 1)
+ *   new token j (row query_start_loc[b] + j) sits at position seq_lens[b]-q_len+j
+ *   and sees keys t <= seq_lens[b] - q_len + j   (causal, bottom-right aligned)
+ *   K_b[t] = key_cache  [block_tables[b][t / bs]][kv][t % bs][:]
+ *   V_b[t] = value_cache[block_tables[b][t / bs]][kv][:][t % bs]
+ *   out[row][h] = sum_t softmax_t(scale * q.K_b[t]) * V_b[t]
+ *
+ * Layouts (all contiguous, row-major):
+ *   query, out      [num_tokens, num_heads, head_dim]
+ *   key, value      [num_tokens, num_kv_heads, head_dim]    (this step's new tokens)
+ *   key_cache       [num_blocks, num_kv_heads, block_size, head_dim]
+ *   value_cache     [num_blocks, num_kv_heads, head_dim, block_size]
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32
+ *   seq_lens        [num_seqs] int32, tokens in the cache INCLUDING this step's
+ *   query_start_loc [num_seqs + 1] int32, prefix sums of query lengths, [0] = 0
+ *
+ * The value page is stored head_dim-major (tokens of a page contiguous per
+ * channel) so that the P.V matrix-core operand is a plain 16-byte load; the key
+ * page is token-major for the same reason on the Q.K^T side.
+ *
+ * Device-data preconditions (not checked on the host; the kernels clamp so that
+ * a violation gives a wrong result, never an out-of-bounds access):
+ *   0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size,
+ *   0 <= block_tables[b][i] < num_blocks for i < ceil(seq_lens[b] / block_size),
+ *   query_start_loc non-decreasing, query_start_loc[num_seqs] == num_tokens,
+ *   q_len <= seq_lens[b].
+ *
+ * Errors: every call returns a gqa_status.  Host-side validation looks at the
+ * scalar arguments only; no exception crosses the ABI.
+ */
+#ifndef GQA_PAGED_H_
+#define GQA_PAGED_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, num_heads % num_kv_heads != 0, ... */
+  GQA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, group size or dtype combination not built */
+  GQA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than *_workspace_size() */
+  GQA_ERR_LAUNCH = 4         /* the HIP runtime reported an error at launch (or no device) */
+} gqa_status;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+typedef struct {
+  int32_t num_seqs;            /* B */
+  int32_t num_heads;           /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;            /* d: 64 or 128 */
+  int32_t block_size;          /* tokens per page: 16 */
+  int32_t num_blocks;          /* pages in each cache */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables */
+  gqa_dtype q_dtype;           /* query (and key/value of reshape_and_cache) */
+  gqa_dtype kv_dtype;          /* caches; must equal q_dtype */
+  gqa_dtype out_dtype;         /* output; accumulation is always fp32 */
+} gqa_dims;
+
+/* Human-readable name of a status code (static storage). */
+const char* gqa_status_string(int32_t status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t gqa_version(void);
+
+/*
+ * reshape_and_cache: copy this step's keys and values into the paged caches.
+ * New token j of sequence b (row query_start_loc[b] + j of key/value) goes to
+ * position pos = seq_lens[b] - q_len + j, i.e. page block_tables[b][pos / bs],
+ * slot pos % bs.  A bit-exact copy in the cache dtype (kv_dtype; key/value are
+ * in kv_dtype too).  Slots not written are left untouched.  num_tokens may be 0
+ * (no launch).  ("[Performance] Use optimized kernels for MQA/GQA", opening
+ * post: incoming keys/values are [tokens, num_kv_heads, head]; item 2: the
+ * decode reads them back from a paged cache.)
+ */
+int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_tokens, gqa_dims dims,
+                          void* stream);
+
+/*
+ * paged_gqa_decode: one query token per sequence (query/out are [num_seqs,
+ * num_heads, head_dim]) attending to all seq_lens[b] cached tokens.  Each
+ * (sequence, kv head) pair reads its K/V pages once for all G query heads of
+ * the group ("[Performance] Use optimized kernels for MQA/GQA", opening post,
+ * item 2).
+ *
+ * partition_size > 0 splits each sequence into partitions of that many tokens
+ * (a multiple of 32) processed by separate work-groups and merged by a
+ * log-sum-exp reduction inside the call; 0 = one partition per sequence.
+ * max_seq_len (host) bounds seq_lens and sizes the grid without a device sync.
+ * seq_lens[b] == 0 gives a zero output row.
+ * The workspace (device, >= paged_gqa_decode_workspace_size bytes, 256-byte
+ * aligned) holds the partials; its contents need no initialisation.
+ */
+size_t paged_gqa_decode_workspace_size(gqa_dims dims, int32_t max_seq_len, int32_t partition_size);
+int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int32_t max_seq_len,
+                         gqa_dims dims, float scale, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * splitk_lse_reduce: merge per-partition decode results.
+ *   partial_out [num_seqs, num_heads, max_partitions, head_dim] fp32: the
+ *                partition's normalised output;
+ *   partial_lse [num_seqs, num_heads, max_partitions] fp32: natural-log
+ *                log-sum-exp of the partition's scaled scores (-inf if empty).
+ * Sequence b has n_b = ceil(seq_lens[b] / partition_size) partitions (clamped
+ * to max_partitions); out[row][h] = sum_{p<n_b} exp(lse_p - LSE) * O_p with
+ * LSE = log sum_p exp(lse_p); zero if every partition is empty.
+ * row = b, or query_start_loc[b] when query_start_loc is non-NULL, in which
+ * case only sequences with exactly one query token are written.
+ * Sequences with n_b <= 1 are skipped when skip_single != 0 (their output is
+ * written directly by the decode kernel), merged otherwise.
+ */
+int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* partial_lse,
+                          const int32_t* seq_lens, const int32_t* query_start_loc, gqa_dims dims,
+                          int32_t max_partitions, int32_t partition_size, int32_t skip_single,
+                          void* stream);
+
+/*
+ * chunked_prefill_paged_decode: attention for a mixed batch of prefill chunks
+ * (q_len > 1, causal within the chunk, bottom-right aligned against the cached
+ * prefix) and decodes (q_len == 1), all over the same paged cache ("[Kernel]
+ * [V1] Further optimizations to ROCm (Triton) Backend to better handle GQA",
+ * review thread: the prefill kernel skips single-token sequences, which a
+ * decode kernel handles).  query/out are [num_tokens, num_heads, head_dim];
+ * max_query_len and max_seq_len are host-side bounds.  Sequences with q_len 0
+ * produce no rows.  Decodes are split into partitions of partition_size tokens
+ * as in paged_gqa_decode (0 = no split).
+ */
+size_t chunked_prefill_paged_decode_workspace_size(gqa_dims dims, int32_t max_seq_len,
+                                                   int32_t partition_size);
+int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, const int32_t* block_tables,
+                                     const int32_t* seq_lens, const int32_t* query_start_loc,
+                                     int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                                     gqa_dims dims, float scale, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* GQA_PAGED_H_ */

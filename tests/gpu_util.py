@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: upload a synthetic batch, call the library
+through its C ABI (via the ctypes binding), and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from gqa_paged_kv_attention_amd import ops
+from gqa_paged_kv_attention_amd import workloads as wl
+
+# Parity bar for bf16 inputs with fp32 accumulation (max-abs and relative L2 over
+# the whole output); fp32 inputs additionally meet a tight relative-L2 guard.
+BF16_MAX_ABS = 1e-2
+BF16_REL_L2 = 2e-3
+F32_REL_L2 = 1e-5
+
+
+def have_gpu() -> bool:
+    return torch.cuda.is_available()
+
+
+class DeviceBatch:
+    def __init__(self, bt: wl.PagedBatch, device="cuda"):
+        self.bt = bt
+        up = lambda a: ops.to_device(a, device)
+        self.query = up(bt.query)
+        self.key_cache = up(bt.key_cache)
+        self.value_cache = up(bt.value_cache)
+        self.new_key = up(bt.new_key)
+        self.new_value = up(bt.new_value)
+        self.block_tables = up(bt.block_tables)
+        self.seq_lens = up(bt.seq_lens)
+        self.query_start_loc = up(bt.query_start_loc)
+
+    def cache_write(self):
+        ops.reshape_and_cache(self.new_key, self.new_value, self.key_cache, self.value_cache, self.block_tables,
+                              self.seq_lens, self.query_start_loc)
+
+    def decode(self, partition_size=0, out_dtype=torch.float32, max_seq_len=None, workspace=None):
+        return ops.paged_gqa_decode(self.query, self.key_cache, self.value_cache, self.block_tables, self.seq_lens,
+                                    self.bt.max_seq_len if max_seq_len is None else max_seq_len, self.bt.scale,
+                                    partition_size=partition_size, out_dtype=out_dtype, workspace=workspace)
+
+    def mixed(self, partition_size=0, out_dtype=torch.float32):
+        return ops.chunked_prefill_paged_decode(self.query, self.key_cache, self.value_cache, self.block_tables,
+                                                self.seq_lens, self.query_start_loc, self.bt.max_query_len,
+                                                self.bt.max_seq_len, self.bt.scale, partition_size=partition_size,
+                                                out_dtype=out_dtype)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def errors(out: np.ndarray, ref: np.ndarray):
+    diff = out - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_parity(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    max_abs, rel = errors(out, ref)
+    msg = f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+    assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, msg
+    if dtype == wl.F32:
+        assert rel <= F32_REL_L2, msg
+    return max_abs, rel
+
+
+def poison_tails(bt: wl.PagedBatch):
+    """NaN into every slot past the end of each sequence's last page."""
+    nan = np.uint16(0x7FC0) if bt.dtype == wl.BF16 else np.float32("nan")
+    for b in range(bt.num_seqs):
+        L = int(bt.seq_lens[b])
+        n = -(-L // bt.block_size)
+        if n == 0:
+            continue
+        used = L - (n - 1) * bt.block_size
+        page = bt.block_tables[b][n - 1]
+        bt.key_cache[page, :, used:, :] = nan
+        bt.value_cache[page, :, :, used:] = nan

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+function include/gqa_paged.h declares, and rejects bad scalar arguments with
+status codes before touching the device."""
+import ctypes
+
+import pytest
+
+from gqa_paged_kv_attention_amd import ops
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ops.load_library()
+
+
+def dims(**kw):
+    base = dict(num_seqs=4, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100,
+                max_blocks_per_seq=16, q_dtype=ops.GQA_BF16, kv_dtype=ops.GQA_BF16, out_dtype=ops.GQA_F32)
+    base.update(kw)
+    return ops.Dims(*[base[f] for f, _ in ops.Dims._fields_])
+
+
+FAKE = ctypes.c_void_p(0x1000)    # never dereferenced: every call below fails validation first
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = ops.declared_functions()
+    assert {"reshape_and_cache", "paged_gqa_decode", "splitk_lse_reduce", "chunked_prefill_paged_decode",
+            "paged_gqa_decode_workspace_size", "chunked_prefill_paged_decode_workspace_size",
+            "gqa_status_string", "gqa_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.gqa_status_string(0) == b"ok"
+    assert lib.gqa_status_string(3) == b"workspace missing or too small"
+    assert lib.gqa_status_string(99) == b"unknown status"
+    assert lib.gqa_version() >= 100
+
+
+def decode(lib, d, max_seq_len=256, partition=0, ws=None, wsb=0, ptr=FAKE, scale=0.1):
+    return lib.paged_gqa_decode(ptr, ptr, ptr, ptr, ptr, ptr, max_seq_len, d, scale, partition, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_kv_heads=7), INVALID),
+    (dict(num_heads=0), INVALID),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(block_size=32), UNSUPPORTED),
+    (dict(q_dtype=ops.GQA_F32), UNSUPPORTED),
+    (dict(out_dtype=7), INVALID),
+    (dict(num_heads=64, num_kv_heads=1), UNSUPPORTED),       # group of 64 > 32
+])
+def test_decode_rejects_bad_dims(lib, kw, expect):
+    assert decode(lib, dims(**kw)) == expect
+
+
+def test_decode_rejects_null_pointer_and_bad_partition(lib):
+    assert decode(lib, dims(), ptr=None) == INVALID
+    assert decode(lib, dims(), partition=48) == INVALID        # not a multiple of 32
+    assert decode(lib, dims(), partition=-32) == INVALID
+    assert decode(lib, dims(), max_seq_len=-1) == INVALID
+    assert decode(lib, dims(), scale=float("nan")) == INVALID
+
+
+def test_workspace_size_and_check(lib):
+    d = dims()
+    assert lib.paged_gqa_decode_workspace_size(d, 256, 0) == 0
+    assert lib.paged_gqa_decode_workspace_size(d, 256, 256) == 0
+    n = lib.paged_gqa_decode_workspace_size(d, 4096, 512)
+    rows = 4 * 32 * 8
+    assert n >= rows * 128 * 4 + rows * 4 and n % 256 == 0
+    assert decode(lib, d, max_seq_len=4096, partition=512) == WORKSPACE
+    assert decode(lib, d, max_seq_len=4096, partition=512, ws=FAKE, wsb=n - 1) == WORKSPACE
+    assert lib.chunked_prefill_paged_decode_workspace_size(d, 4096, 512) == n
+
+
+def test_empty_batches_return_ok_without_launch(lib):
+    assert decode(lib, dims(num_seqs=0), ptr=None) == OK
+    assert lib.reshape_and_cache(None, None, None, None, None, None, None, 0, dims(), None) == OK
+    assert lib.chunked_prefill_paged_decode(None, None, None, None, None, None, None, 0, 0, 0, dims(), 0.1, 0,
+                                            None, 0, None) == OK
+
+
+def test_mixed_and_reduce_validation(lib):
+    d = dims()
+    assert lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 20, 10, d, 0.1, 0,
+                                            None, 0, None) == INVALID        # max_query_len > max_seq_len
+    assert lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 10, 5, 10, d, 0.1, 0,
+                                            None, 0, None) == INVALID        # no query_start_loc
+    assert lib.reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, d, None) == INVALID
+    assert lib.splitk_lse_reduce(FAKE, FAKE, FAKE, FAKE, None, d, 0, 512, 1, None) == INVALID
+    assert lib.splitk_lse_reduce(FAKE, FAKE, FAKE, FAKE, None, d, 4, 0, 1, None) == INVALID

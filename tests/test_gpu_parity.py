@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Small cases compare every output element; full-size workloads (the shapes and
+launch configuration the benchmark times) compare sampled sequences that the
+oracle computes one by one.  The bar: max-abs <= 1e-2 and relative L2 <= 2e-3
+for bf16 inputs with fp32 accumulation; fp32 inputs also meet relative L2 <=
+1e-5; the cache write is bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gqa_paged_kv_attention_amd import ops
+from gqa_paged_kv_attention_amd import workloads as wl
+from oracle import cache_write_ref, decode_ref, lse_merge_ref, paged_attention_ref
+from tests.gpu_util import DeviceBatch, assert_parity, have_gpu, host, poison_tails
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def oracle_after_write(bt, seqs=None, mixed=False):
+    kc, vc = cache_write_ref(bt.new_key, bt.new_value, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                             bt.query_start_loc)
+    if mixed:
+        return paged_attention_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.query_start_loc,
+                                   bt.num_kv_heads, bt.scale, seqs=seqs)
+    return decode_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.num_kv_heads, bt.scale, seqs=seqs)
+
+
+def decode_step(bt, partition_size, out_dtype=torch.float32):
+    d = DeviceBatch(bt)
+    d.cache_write()
+    return host(d.decode(partition_size, out_dtype=out_dtype))
+
+
+def mixed_step(bt, partition_size, out_dtype=torch.float32):
+    d = DeviceBatch(bt)
+    d.cache_write()
+    return host(d.mixed(partition_size, out_dtype=out_dtype))
+
+
+# --------------------------------------------------------------------------
+# reshape_and_cache: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reshape_and_cache_bit_exact(dtype, d):
+    rng = np.random.default_rng(7)
+    q_lens = np.array([1, 5, 0, 17, 1, 33, 2])
+    seq_lens = q_lens + rng.integers(0, 40, size=len(q_lens))
+    bt = wl.make_batch(name="rc", seed=8, num_heads=8, num_kv_heads=4, head_dim=d, block_size=16,
+                       seq_lens=seq_lens, query_lens=q_lens, dtype=dtype)
+    dev = DeviceBatch(bt)
+    dev.cache_write()
+    torch.cuda.synchronize()
+    kc, vc = cache_write_ref(bt.new_key, bt.new_value, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                             bt.query_start_loc)
+    assert np.array_equal(ops.to_host_storage(dev.key_cache).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(ops.to_host_storage(dev.value_cache).view(np.uint8), vc.view(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# decode: small workloads, full oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [1, 101, 102, 103])
+@pytest.mark.parametrize("partition", [0, 32, 64])
+def test_tiny_decode_fp32(seed, partition):
+    bt = wl.tiny_decode(seed)
+    assert_parity(decode_step(bt, partition), oracle_after_write(bt), bt.dtype, bt.describe())
+
+
+@pytest.mark.parametrize("partition", [0, 64, 512])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_llama31_decode_small(partition, out_dtype):
+    bt = wl.llama31_8b_decode(seed=2, num_seqs=10)
+    out = decode_step(bt, partition, out_dtype)
+    ref = oracle_after_write(bt)
+    if out_dtype == torch.bfloat16:
+        # bf16 output rounding alone is ~1.7e-3 relative; check it against the
+        # fp32-output kernel rounded to bf16 (at most one bf16 ulp apart)
+        f32 = decode_step(bt, partition, torch.float32)
+        rounded = torch.from_numpy(f32).to(torch.bfloat16).double().numpy()
+        ulp = np.abs(rounded) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(out - rounded) <= ulp)
+        assert np.max(np.abs(out - ref)) <= 1e-2
+    else:
+        assert_parity(out, ref, bt.dtype, bt.describe())
+
+
+@pytest.mark.parametrize("hkv", [32, 8, 1])
+def test_llama2_sweep_small(hkv):
+    bt = wl.llama2_7b_sweep(hkv, seed=3, num_seqs=12)
+    assert_parity(decode_step(bt, 256), oracle_after_write(bt), bt.dtype, bt.describe())
+
+
+def test_longctx_small():
+    bt = wl.longctx_splitk(seed=5, num_seqs=2, ctx=4000)
+    assert_parity(decode_step(bt, wl.LONGCTX_PARTITION), oracle_after_write(bt), bt.dtype, bt.describe())
+
+
+# --------------------------------------------------------------------------
+# decode edge cases
+# --------------------------------------------------------------------------
+
+EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 511, 512, 513]
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (6, 2), (8, 2), (10, 2), (16, 2), (16, 1), (32, 2), (32, 1)])
+def test_decode_edge_shapes(dtype, d, hq, hkv):
+    bt = wl.make_batch(name="edge", seed=hq * 100 + hkv + d, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       block_size=16, seq_lens=EDGE_LENS, query_lens=[0 if L == 0 else 1 for L in EDGE_LENS],
+                       dtype=dtype, poison_slack=True)
+    poison_tails(bt)
+    # zero-length sequences have no query token; give them a query row anyway (decode is one row per sequence)
+    q = wl._normal_storage(np.random.default_rng(0), (len(EDGE_LENS), hq, d), dtype)
+    bt.query = q
+    dev = DeviceBatch(bt)
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, hkv, bt.scale)
+    for partition in (0, 32, 96):
+        out = host(dev.decode(partition))
+        assert_parity(out, ref, dtype, f"{bt.describe()} P={partition}")
+        assert np.all(out[0] == 0)          # empty sequence -> zero row
+
+
+def test_decode_peaky_scores_exercise_rescale():
+    """Scores far from uniform (q scaled up) so the running max moves across tiles."""
+    bt = wl.llama31_8b_decode(seed=9, num_seqs=6, ctx_lo=100, ctx_hi=1500)
+    qf = wl.bf16_bits_to_f32(bt.query) * 4.0
+    bt.query = wl.f32_to_bf16_bits(qf)
+    for partition in (0, 128):
+        assert_parity(decode_step(bt, partition), oracle_after_write(bt), bt.dtype, f"peaky P={partition}")
+
+
+def test_decode_is_deterministic():
+    bt = wl.llama31_8b_decode(seed=11, num_seqs=16)
+    dev = DeviceBatch(bt)
+    a = dev.decode(256).cpu()
+    b = dev.decode(256).cpu()
+    assert torch.equal(a, b)
+
+
+def test_split_invariance():
+    bt = wl.llama31_8b_decode(seed=12, num_seqs=8, ctx_lo=900, ctx_hi=2100)
+    dev = DeviceBatch(bt)
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
+                     bt.scale)
+    outs = [host(dev.decode(p)) for p in (0, 32, 64, 160, 512, 2048)]
+    for o in outs:
+        assert_parity(o, ref, bt.dtype)
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# split-K reduce on its own
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("use_qsl", [False, True])
+def test_splitk_lse_reduce_random_partials(use_qsl):
+    rng = np.random.default_rng(21)
+    B, Hq, P, d, psize = 6, 8, 5, 128, 64
+    seq_lens = np.array([0, 1, 64, 65, 200, 320], np.int32)
+    O = rng.standard_normal((B, Hq, P, d)).astype(np.float32)
+    lse = (rng.standard_normal((B, Hq, P)) * 3).astype(np.float32)
+    nparts = np.minimum(-(-seq_lens // psize), P)
+    for b in range(B):
+        lse[b, :, nparts[b]:] = -np.inf        # partitions past the sequence are never read
+        O[b, :, nparts[b]:] = np.nan
+    lse[4, 3, 1] = -np.inf                      # an empty partition inside a sequence
+    ref = np.zeros((B, Hq, d))
+    for b in range(B):
+        if nparts[b] > 0:
+            ref[b] = lse_merge_ref(O[b, :, :nparts[b]].astype(np.float64), lse[b, :, :nparts[b]].astype(np.float64))
+    qsl = None
+    rows = B
+    if use_qsl:
+        q_lens = np.ones(B, np.int32)
+        q_lens[2] = 3                            # not a decode: must be left alone
+        qsl_h = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        qsl = torch.from_numpy(qsl_h).cuda()
+        rows = int(qsl_h[-1])
+    out = ops.splitk_lse_reduce(torch.from_numpy(O).cuda(), torch.from_numpy(lse).cuda(),
+                                torch.from_numpy(seq_lens).cuda(), psize, num_kv_heads=2, max_blocks_per_seq=32,
+                                query_start_loc=qsl, num_out_rows=rows)
+    got = host(out)
+    if use_qsl:
+        for b in range(B):
+            if b == 2:
+                assert np.all(got[qsl_h[b]:qsl_h[b + 1]] == 0)
+            else:
+                np.testing.assert_allclose(got[qsl_h[b]], ref[b], rtol=0, atol=2e-6)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6)
+
+
+# --------------------------------------------------------------------------
+# mixed chunked-prefill + decode
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("partition", [0, 128])
+def test_mixed_small(partition):
+    bt = wl.mixed_chunked(seed=4, num_seqs=30, token_budget=1200)
+    assert_parity(mixed_step(bt, partition), oracle_after_write(bt, mixed=True), bt.dtype, bt.describe())
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (32, 1), (12, 2), (16, 1)])
+def test_mixed_edge_shapes(dtype, d, hq, hkv):
+    q_lens = [2, 1, 0, 7, 33, 1, 64, 130, 5, 1, 16]
+    prior = [0, 40, 3, 9, 0, 300, 17, 70, 511, 0, 16]
+    seq_lens = [a + b for a, b in zip(q_lens, prior)]
+    bt = wl.make_batch(name="medge", seed=hq + 7 * hkv + d, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       block_size=16, seq_lens=seq_lens, query_lens=q_lens, dtype=dtype, poison_slack=True)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, hkv, bt.scale)
+    for partition in (0, 64):
+        assert_parity(host(dev.mixed(partition)), ref, dtype, f"{bt.describe()} P={partition}")
+
+
+def test_prefill_chunk_invariance_on_gpu():
+    """A 96-token chunk equals three sequential 32-token chunks over the same cache."""
+    L, C = 400, 96
+    full = wl.make_batch(name="chunk", seed=33, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                         seq_lens=[L], query_lens=[C], dtype=wl.BF16)
+    dev = DeviceBatch(full)
+    whole = host(dev.mixed())
+    parts = []
+    for c in range(3):
+        qsl = torch.tensor([0, 32], dtype=torch.int32, device="cuda")
+        sl = torch.tensor([L - C + 32 * (c + 1)], dtype=torch.int32, device="cuda")
+        parts.append(host(ops.chunked_prefill_paged_decode(dev.query[32 * c:32 * (c + 1)].contiguous(), dev.key_cache,
+                                                           dev.value_cache, dev.block_tables, sl, qsl, 32,
+                                                           L - C + 32 * (c + 1), full.scale)))
+    assert np.max(np.abs(np.concatenate(parts) - whole)) <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, sampled sequences (benchmark launch configuration)
+# --------------------------------------------------------------------------
+
+def sampled(bt, k, seed):
+    rng = np.random.default_rng(seed)
+    order = np.argsort(bt.seq_lens)
+    picks = {int(order[0]), int(order[-1])}
+    picks |= set(int(x) for x in rng.choice(bt.num_seqs, size=min(k, bt.num_seqs), replace=False))
+    return sorted(picks)
+
+
+def check_rows(out, ref, rows, dtype, what):
+    assert np.isfinite(out).all(), what
+    assert_parity(out[rows], ref[rows], dtype, what)
+
+
+def test_full_llama31_decode_sampled():
+    bt = wl.llama31_8b_decode(seed=2)
+    seqs = sampled(bt, 6, 0)
+    out = decode_step(bt, 512)
+    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
+
+
+@pytest.mark.parametrize("hkv", [32, 8, 1])
+def test_full_llama2_sweep_sampled(hkv):
+    bt = wl.llama2_7b_sweep(hkv, seed=3)
+    seqs = sampled(bt, 5, hkv)
+    out = decode_step(bt, 256)
+    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
+
+
+def test_full_mixed_sampled():
+    bt = wl.mixed_chunked(seed=4)
+    seqs = sampled(bt, 8, 4)
+    big = int(np.argmax(bt.query_lens))
+    seqs = sorted(set(seqs) | {big})
+    out = mixed_step(bt, 512)
+    ref = oracle_after_write(bt, seqs=seqs, mixed=True)
+    rows = np.concatenate([np.arange(bt.query_start_loc[b], bt.query_start_loc[b + 1]) for b in seqs])
+    check_rows(out, ref, rows, bt.dtype, bt.describe())
+
+
+def test_full_longctx_splitk_sampled():
+    bt = wl.longctx_splitk(seed=5)
+    seqs = [0, 7, 15]
+    out = decode_step(bt, wl.LONGCTX_PARTITION)
+    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
