@@ -33,8 +33,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition", type=int, default=512)
-    ap.add_argument("--mixed-partition", type=int, default=512)
+    ap.add_argument("--partition", type=int, default=0, help="0 = library picks (balanced split)")
+    ap.add_argument("--mixed-partition", type=int, default=0)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
@@ -137,7 +137,7 @@ def main():
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "paged_gqa_decode (decode + split-K merge)", "avg_ms": round(decode_ms, 5),
+                "kernel": "paged_gqa_decode call (balanced decode kernel + merge kernel)", "avg_ms": round(decode_ms, 5),
                 "bytes_per_launch": kv_bytes}
 
     record = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -46,6 +46,8 @@ bool partitioning(int32_t max_seq_len, int32_t partition_size, int* psize, int* 
   return true;
 }
 
+// Fixed-partition workspace: [partial_out][partial_lse]; nothing when every
+// sequence fits one partition.
 size_t partial_bytes(const gqa_dims& d, int nparts) {
   if (nparts <= 1) return 0;
   const size_t rows = (size_t)d.num_seqs * d.num_heads * nparts;
@@ -54,6 +56,45 @@ size_t partial_bytes(const gqa_dims& d, int nparts) {
 
 int status_from(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH; }
 
+int device_workers(const gqa_dims& d);
+
+// partition_size == 0 picks the decomposition.  The balanced (stream) decode
+// pays a merge kernel and per-segment restarts, which only win when the batch
+// has too few (sequence, kv head) units to balance itself over the device's
+// resident work-groups; with many units, or G > 16 (a segment then weighs as
+// much as a tile), one work-group per unit is faster.  The stream kernel also
+// needs the batch to fit its LDS table and the tile count to fit in 32 bits.
+bool use_stream(const gqa_dims& d, int32_t partition_size) {
+  if (partition_size != 0 || d.num_seqs == 0 || d.num_seqs > gqa::kMaxStreamSeqs) return false;
+  if (d.num_heads / d.num_kv_heads > 16) return false;
+  const long long tiles_per_seq = ((long long)d.max_blocks_per_seq * d.block_size + kTileTokens - 1) / kTileTokens;
+  if ((long long)d.num_seqs * d.num_kv_heads * tiles_per_seq >= (1LL << 31) - 1) return false;
+  const long long resident_groups = device_workers(d) / gqa::kStreamWorkersPerGroup;
+  return (long long)d.num_seqs * d.num_kv_heads < 2 * resident_groups;
+}
+
+// Balanced-decode workspace: [tile prefix, B + 1 ints][unit metadata, B * Hkv int4]
+// [segment outputs][segment lse].
+size_t stream_bytes(const gqa_dims& d, int workers) {
+  const int G = d.num_heads / d.num_kv_heads;
+  const size_t segs = (size_t)workers * 2 * G;
+  return align_up((size_t)(d.num_seqs + 1) * sizeof(int)) +
+         align_up((size_t)d.num_seqs * d.num_kv_heads * 4 * sizeof(int)) + align_up(segs * d.head_dim * sizeof(float)) +
+         align_up(segs * sizeof(float));
+}
+
+int device_workers(const gqa_dims& d) {
+  return gqa::stream_workers(d.head_dim, d.kv_dtype == GQA_F32, d.out_dtype == GQA_F32,
+                             d.num_heads / d.num_kv_heads, d.num_seqs);
+}
+
+size_t decode_workspace(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
+  if (use_stream(d, partition_size)) return stream_bytes(d, device_workers(d));
+  int psize = 0, nparts = 0;
+  if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return 0;
+  return partial_bytes(d, nparts);
+}
+
 // Decode launch shared by paged_gqa_decode and the decode half of the mixed call.
 int run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
@@ -61,10 +102,51 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int psize = 0, nparts = 0;
   if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
+  const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
+  const float scale_log2 = scale * 1.4426950408889634f;
+
+  if (use_stream(dims, partition_size)) {
+    if (workspace == nullptr) return GQA_ERR_WORKSPACE;
+    // as many workers as the device holds at once, fewer if the workspace is smaller
+    int workers = device_workers(dims);
+    while (workers > gqa::kStreamWorkersPerGroup && stream_bytes(dims, workers) > workspace_bytes)
+      workers -= gqa::kStreamWorkersPerGroup;
+    if (stream_bytes(dims, workers) > workspace_bytes) return GQA_ERR_WORKSPACE;
+    const int G = dims.num_heads / dims.num_kv_heads;
+    char* ws = reinterpret_cast<char*>(workspace);
+    const size_t segs = (size_t)workers * 2 * G;
+    gqa::StreamArgs a;
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.query_start_loc = query_start_loc;
+    a.tile_prefix = reinterpret_cast<int*>(ws);
+    ws += align_up((size_t)(dims.num_seqs + 1) * sizeof(int));
+    a.unit_meta = reinterpret_cast<int4*>(ws);
+    ws += align_up((size_t)dims.num_seqs * dims.num_kv_heads * 4 * sizeof(int));
+    a.seg_out = reinterpret_cast<float*>(ws);
+    ws += align_up(segs * dims.head_dim * sizeof(float));
+    a.seg_lse = reinterpret_cast<float*>(ws);
+    a.num_seqs = dims.num_seqs;
+    a.num_heads = dims.num_heads;
+    a.num_kv_heads = dims.num_kv_heads;
+    a.group = G;
+    a.num_blocks = dims.num_blocks;
+    a.max_blocks_per_seq = dims.max_blocks_per_seq;
+    a.num_tokens = num_tokens;
+    a.num_workers = workers;
+    a.scale_log2 = scale_log2;
+    hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, kv_f32, out_f32, stream);
+    if (e != hipSuccess) return GQA_ERR_LAUNCH;
+    return status_from(gqa::launch_stream_reduce(a, dims.head_dim, out_f32, stream));
+  }
+
   const size_t need = partial_bytes(dims, nparts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
   if (dims.num_seqs == 0) return GQA_OK;
-
   gqa::DecodeArgs a;
   a.out = out;
   a.query = query;
@@ -74,10 +156,9 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   a.seq_lens = seq_lens;
   a.query_start_loc = query_start_loc;
   const size_t rows = (size_t)dims.num_seqs * dims.num_heads * nparts;
-  a.partial_out = need ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.partial_lse = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                                   align_up(rows * dims.head_dim * sizeof(float)))
-                       : nullptr;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.partial_out = need ? reinterpret_cast<float*>(ws) : nullptr;
+  a.partial_lse = need ? reinterpret_cast<float*>(ws + align_up(rows * dims.head_dim * sizeof(float))) : nullptr;
   a.num_heads = dims.num_heads;
   a.num_kv_heads = dims.num_kv_heads;
   a.group = dims.num_heads / dims.num_kv_heads;
@@ -86,26 +167,24 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   a.num_tokens = num_tokens;
   a.partition_size = psize;
   a.max_partitions = nparts;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
+  a.scale_log2 = scale_log2;
   hipError_t e = gqa::launch_decode(a, dims.head_dim, kv_f32, out_f32, dims.num_seqs, stream);
-  if (e != hipSuccess) return GQA_ERR_LAUNCH;
-  if (nparts > 1) {
-    gqa::ReduceArgs r;
-    r.out = out;
-    r.partial_out = a.partial_out;
-    r.partial_lse = a.partial_lse;
-    r.seq_lens = seq_lens;
-    r.query_start_loc = query_start_loc;
-    r.num_heads = dims.num_heads;
-    r.max_blocks_per_seq = dims.max_blocks_per_seq;
-    r.max_partitions = nparts;
-    r.partition_size = psize;
-    r.num_tokens = num_tokens;
-    r.skip_single = 1;
-    e = gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, stream);
-  }
-  return status_from(e);
+  if (e != hipSuccess || nparts <= 1) return status_from(e);
+  gqa::ReduceArgs r;
+  r.out = out;
+  r.partial_out = a.partial_out;
+  r.partial_lse = a.partial_lse;
+  r.seq_lens = seq_lens;
+  r.query_start_loc = query_start_loc;
+  r.num_heads = dims.num_heads;
+  r.num_kv_heads = dims.num_kv_heads;
+  r.group = a.group;
+  r.max_blocks_per_seq = dims.max_blocks_per_seq;
+  r.max_partitions = nparts;
+  r.partition_size = psize;
+  r.num_tokens = num_tokens;
+  r.skip_single = 1;
+  return status_from(gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, stream));
 }
 
 }  // namespace
@@ -152,9 +231,8 @@ int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, v
 }
 
 size_t paged_gqa_decode_workspace_size(gqa_dims dims, int32_t max_seq_len, int32_t partition_size) {
-  int psize = 0, nparts = 0;
-  if (check_dims(dims) != GQA_OK || !partitioning(max_seq_len, partition_size, &psize, &nparts)) return 0;
-  return partial_bytes(dims, nparts);
+  if (check_dims(dims) != GQA_OK) return 0;
+  return decode_workspace(dims, max_seq_len, partition_size);
 }
 
 int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -178,6 +256,7 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
   int st = check_dims(dims);
   if (st != GQA_OK) return st;
   if (max_partitions <= 0 || partition_size <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
   if (dims.num_seqs == 0) return GQA_OK;
   if (!out || !partial_out || !partial_lse || !seq_lens) return GQA_ERR_INVALID_ARG;
   gqa::ReduceArgs r;
@@ -187,6 +266,8 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
   r.seq_lens = seq_lens;
   r.query_start_loc = query_start_loc;
   r.num_heads = dims.num_heads;
+  r.num_kv_heads = dims.num_kv_heads;
+  r.group = dims.num_heads / dims.num_kv_heads;
   r.max_blocks_per_seq = dims.max_blocks_per_seq;
   r.max_partitions = max_partitions;
   r.partition_size = partition_size;
@@ -220,8 +301,13 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
   {
     int ps = 0, np = 0;
     if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
-    const size_t need = partial_bytes(dims, np);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+    if (use_stream(dims, partition_size)) {
+      if (workspace == nullptr || workspace_bytes < stream_bytes(dims, gqa::kStreamWorkersPerGroup))
+        return GQA_ERR_WORKSPACE;
+    } else {
+      const size_t need = partial_bytes(dims, np);
+      if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+    }
   }
   if (max_query_len > 1) {
     gqa::PrefillArgs p;

@@ -107,6 +107,7 @@ __device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_b
 //    P.V product keeps fp32-grade weights.
 template <int D>
 struct TileBF16 {
+  static constexpr bool kPipelined = true;  // double-buffered tile loop
   static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
   static constexpr int DT = D / 16;   // 16-channel blocks of the output
   struct K { uint4 v[2][KC]; };
@@ -207,6 +208,11 @@ struct TileBF16 {
 //    4q + i), whose B operand is the lane's own score for that token.
 template <int D>
 struct TileF32 {
+  // Single-buffered tile loop: with the double-buffered loop and a work-group
+  // stride of 4 tiles, fp32 head_dim 64 produced wrong results on gfx950 while
+  // the single-buffered loop is exact; fp32 is the reference-precision path,
+  // not the bandwidth path, so it keeps the simple loop.
+  static constexpr bool kPipelined = false;
   static constexpr int KC = D / 16;
   static constexpr int DT = D / 16;
   struct K { float4 v[2][KC]; };

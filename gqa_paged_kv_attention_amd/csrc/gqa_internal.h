@@ -6,6 +6,7 @@
 
 namespace gqa {
 
+// Fixed-partition decode (one work-group per (partition, kv head, sequence)).
 struct DecodeArgs {
   void* out;
   const void* query;
@@ -25,6 +26,33 @@ struct DecodeArgs {
   int partition_size;               // tokens per partition, multiple of 32
   int max_partitions;
   float scale_log2;                 // scale * log2(e)
+};
+
+// Balanced ("stream") decode: persistent waves, each owning an equal slice of
+// the list of (sequence, kv head, 32-token tile) work items.
+constexpr int kMaxStreamSeqs = 15871;   // prefix table fits 62 KiB of LDS
+constexpr int kStreamWorkersPerGroup = 4;
+struct StreamArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;   // nullptr: pure decode
+  int* tile_prefix;                 // [B + 1]: prefix of tiles * Hkv (work-group 0 writes it)
+  int4* unit_meta;                  // [B * Hkv]: {first worker, last worker, first slot, out row}
+  float* seg_out;                   // [num_workers, 2, G, D]: cut segments, normalised
+  float* seg_lse;                   // [num_workers, 2, G]
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int num_tokens;
+  int num_workers;                  // 4 per work-group
+  float scale_log2;
 };
 
 struct PrefillArgs {
@@ -52,6 +80,8 @@ struct ReduceArgs {
   const int32_t* seq_lens;
   const int32_t* query_start_loc;
   int num_heads;
+  int num_kv_heads;
+  int group;
   int max_blocks_per_seq;
   int max_partitions;
   int partition_size;
@@ -77,6 +107,10 @@ struct CacheWriteArgs {
 // kv_f32 / out_f32 select fp32 (true) or bf16 (false) storage.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool kv_f32, bool out_f32, int num_seqs,
                          hipStream_t stream);
+// Workers (4 per work-group) that fill the device at full occupancy.
+int stream_workers(int head_dim, bool kv_f32, bool out_f32, int group, int num_seqs);
+hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream);
+hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream);
 // Rows per prefill work-group (depends only on the build).
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,

@@ -14,27 +14,46 @@ namespace gqa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kLdsSeqs = 4095;          // query_start_loc staged in LDS up to this many sequences
 
 // One thread per (token, kv head, 16-byte chunk of the head): VEC elements.
+// The work-group stages query_start_loc in LDS (one parallel load) so that
+// each thread finds its sequence by a binary search in LDS rather than a chain
+// of dependent global loads; beyond kLdsSeqs sequences it searches in memory.
 template <int D, class T>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CH = D / VEC;
+  __shared__ int s_qsl[kLdsSeqs + 1];
+  const bool staged = a.num_seqs <= kLdsSeqs;
+  if (staged)
+    for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) s_qsl[i] = a.query_start_loc[i];
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long per_tok = (long long)a.num_kv_heads * CH;
-  if (gid >= (long long)a.num_tokens * per_tok) return;
-  const int tok = (int)(gid / per_tok);
-  const int rem = (int)(gid % per_tok);
+  const bool active = gid < (long long)a.num_tokens * per_tok;
+  const int tok = active ? (int)(gid / per_tok) : 0;
+  const int rem = active ? (int)(gid % per_tok) : 0;
   const int kv = rem / CH, c = rem % CH;
+  // the source row does not depend on the sequence: start its loads early
+  const size_t src = ((size_t)tok * a.num_kv_heads + kv) * D + c * VEC;
+  uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+  if (active) {
+    kx = ld16(reinterpret_cast<const T*>(a.key) + src);
+    vx = ld16(reinterpret_cast<const T*>(a.value) + src);
+  }
+  __syncthreads();
+  if (!active) return;
 
   // sequence owning this token: last b with query_start_loc[b] <= tok
   int lo = 0, hi = a.num_seqs;           // invariant: qsl[lo] <= tok < qsl[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.query_start_loc[mid] <= tok) lo = mid; else hi = mid;
+    const int v = staged ? s_qsl[mid] : a.query_start_loc[mid];
+    if (v <= tok) lo = mid; else hi = mid;
   }
   const int b = lo;
-  const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+  const int q0 = staged ? s_qsl[b] : a.query_start_loc[b];
+  const int q1 = staged ? s_qsl[b + 1] : a.query_start_loc[b + 1];
   if (tok < q0 || tok >= q1) return;
   const int pos = a.seq_lens[b] - (q1 - q0) + (tok - q0);
   if (pos < 0 || pos >= a.max_blocks_per_seq * kPage) return;
@@ -42,12 +61,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
   if ((unsigned)page >= (unsigned)a.num_blocks) return;
   const int slot = pos % kPage;
 
-  const size_t src = ((size_t)tok * a.num_kv_heads + kv) * D + c * VEC;
   const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)(kPage * D);
-  const uint4 kx = ld16(reinterpret_cast<const T*>(a.key) + src);
   *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.key_cache) + pbase + (size_t)slot * D + c * VEC) = kx;
-
-  const uint4 vx = ld16(reinterpret_cast<const T*>(a.value) + src);
   T vals[VEC];
   __builtin_memcpy(vals, &vx, 16);
   T* vdst = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)(c * VEC) * kPage + slot;

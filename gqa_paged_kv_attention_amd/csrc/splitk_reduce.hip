@@ -12,52 +12,60 @@ namespace gqa {
 
 namespace {
 
-// grid (Hq, B), one wave; lane handles channels lane, lane + 64, ...
+constexpr int kUnroll = 8;
+
+// grid (Hq, B), one thread per output channel; partitions are folded kUnroll
+// at a time with independent loads and an online log-sum-exp.
 template <int D, class OutT>
-__global__ __launch_bounds__(kWave) void splitk_reduce_kernel(ReduceArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(D) void splitk_reduce_kernel(ReduceArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   int row = b;
   if (a.query_start_loc) {
     const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
     if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
     row = q0;
   }
-  int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_blocks_per_seq * kPage));
+  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
   const int n = min((L + a.partition_size - 1) / a.partition_size, a.max_partitions);
   if (a.skip_single && n <= 1) return;
-
   const size_t hb = (size_t)b * a.num_heads + h;
   const float* lse = a.partial_lse + hb * a.max_partitions;
-  const float* po = a.partial_out + hb * a.max_partitions * D;
-  OutT* out = reinterpret_cast<OutT*>(a.out) + ((size_t)row * a.num_heads + h) * D;
-
-  float M = -INFINITY;
-  for (int p = 0; p < n; ++p) M = fmaxf(M, lse[p]);
-  if (M == -INFINITY) {
-    for (int d = threadIdx.x; d < D; d += kWave) store1(out + d, 0.f);
-    return;
-  }
-  float den = 0.f;
-  for (int p = 0; p < n; ++p) den += fast_exp2((lse[p] - M) * kLog2e);
-  const float inv = 1.f / den;
-  for (int d = threadIdx.x; d < D; d += kWave) {
-    float acc = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const float w = fast_exp2((lse[p] - M) * kLog2e);
-      if (w != 0.f) acc += w * po[(size_t)p * D + d];
+  const float* po = a.partial_out + hb * a.max_partitions * D + d;
+  float M = -INFINITY, den = 0.f, acc = 0.f;
+  for (int p = 0; p < n; p += kUnroll) {
+    float lv[kUnroll], ov[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      lv[u] = p + u < n ? lse[p + u] : -INFINITY;
+      ov[u] = p + u < n ? po[(size_t)(p + u) * D] : 0.f;
     }
-    store1(out + d, acc * inv);
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) bm = fmaxf(bm, lv[u]);
+    const float nm = fmaxf(M, bm);
+    const float nu = (nm == -INFINITY) ? 0.f : nm;
+    const float r = fast_exp2((M - nu) * kLog2e);
+    den *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float w = fast_exp2((lv[u] - nu) * kLog2e);
+      den += w;
+      acc += w == 0.f ? 0.f : w * ov[u];
+    }
+    M = nm;
   }
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  store1(out + ((size_t)row * a.num_heads + h) * D + d, den > 0.f ? acc / den : 0.f);
 }
 
 template <class OutT>
 hipError_t dispatch(const ReduceArgs& a, int D, int num_seqs, hipStream_t s) {
   dim3 grid(a.num_heads, num_seqs);
   if (D == 64)
-    hipLaunchKernelGGL((splitk_reduce_kernel<64, OutT>), grid, dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL((splitk_reduce_kernel<64, OutT>), grid, dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL((splitk_reduce_kernel<128, OutT>), grid, dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL((splitk_reduce_kernel<128, OutT>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

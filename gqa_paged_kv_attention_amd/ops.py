@@ -156,9 +156,10 @@ def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace too small: need {nbytes} bytes")
+        # the leading counter area must start at zero; every call leaves it zero
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    # a smaller workspace is passed through: the library either adapts (balanced
+    # split: fewer waves) or returns GQA_ERR_WORKSPACE
     return workspace, workspace.numel() * workspace.element_size()
 
 

@@ -114,13 +114,34 @@ int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, v
  * the group ("[Performance] Use optimized kernels for MQA/GQA", opening post,
  * item 2).
  *
- * partition_size > 0 splits each sequence into partitions of that many tokens
- * (a multiple of 32) processed by separate work-groups and merged by a
- * log-sum-exp reduction inside the call; 0 = one partition per sequence.
- * max_seq_len (host) bounds seq_lens and sizes the grid without a device sync.
+ * partition_size == 0 (recommended): the library picks the split.  When the
+ * batch has fewer (sequence, kv head) units than twice the device's resident
+ * work-groups and G <= 16, it uses a balanced split: the (sequence, kv head,
+ * 32-token tile) work items of the whole batch are divided into equal
+ * contiguous ranges, one per resident wave, so every wave streams the same
+ * number of K/V bytes whatever the mix of context lengths; a (sequence, kv
+ * head) whose keys fall in one range is finished by that wave, one cut by
+ * range boundaries is merged by log-sum-exp in a second, small kernel, in a
+ * fixed order (results are reproducible on a given device).  Otherwise (many
+ * units, G > 16, num_seqs > 15871, or more than 2^31 tiles) each (sequence,
+ * kv head) is one work-group's job, with no split.
+ *
+ * partition_size > 0: fixed split-K.  Each sequence of L tokens is split into
+ * ceil(L / partition_size) partitions of nearly equal length (whole 32-token
+ * tiles; partition_size must be a multiple of 32), each processed by one
+ * work-group; partials are merged by log-sum-exp in partition order by a
+ * second kernel.  partition_size >= max_seq_len means no split.
+ *
+ * The result does not depend on the split beyond fp32 rounding.  max_seq_len
+ * (host) bounds seq_lens and sizes the grid without a device sync.
  * seq_lens[b] == 0 gives a zero output row.
- * The workspace (device, >= paged_gqa_decode_workspace_size bytes, 256-byte
- * aligned) holds the partials; its contents need no initialisation.
+ *
+ * Workspace (device, >= paged_gqa_decode_workspace_size bytes, 256-byte
+ * aligned; may be NULL when that size is 0): scratch for the split partials;
+ * its contents need no initialisation and are meaningless between calls.  For
+ * the balanced split the size depends on the current device's compute-unit
+ * count and occupancy; a smaller (but non-zero) workspace is accepted and uses
+ * fewer waves.
  */
 size_t paged_gqa_decode_workspace_size(gqa_dims dims, int32_t max_seq_len, int32_t partition_size);
 int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -139,8 +160,10 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
  * LSE = log sum_p exp(lse_p); zero if every partition is empty.
  * row = b, or query_start_loc[b] when query_start_loc is non-NULL, in which
  * case only sequences with exactly one query token are written.
- * Sequences with n_b <= 1 are skipped when skip_single != 0 (their output is
- * written directly by the decode kernel), merged otherwise.
+ * Sequences with n_b <= 1 are skipped when skip_single != 0, merged
+ * otherwise.  (paged_gqa_decode merges its own partials in-kernel; this entry
+ * point serves partials produced elsewhere, e.g. one per device of a
+ * sequence-sharded decode.)
  */
 int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* partial_lse,
                           const int32_t* seq_lens, const int32_t* query_start_loc, gqa_dims dims,

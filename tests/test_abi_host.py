@@ -68,14 +68,21 @@ def test_decode_rejects_null_pointer_and_bad_partition(lib):
 
 def test_workspace_size_and_check(lib):
     d = dims()
-    assert lib.paged_gqa_decode_workspace_size(d, 256, 0) == 0
+    # no split: nothing needed
     assert lib.paged_gqa_decode_workspace_size(d, 256, 256) == 0
+    assert lib.paged_gqa_decode_workspace_size(d, 200, 1024) == 0
+    # fixed split: partials for 8 partitions of every (sequence, query head)
     n = lib.paged_gqa_decode_workspace_size(d, 4096, 512)
     rows = 4 * 32 * 8
     assert n >= rows * 128 * 4 + rows * 4 and n % 256 == 0
     assert decode(lib, d, max_seq_len=4096, partition=512) == WORKSPACE
     assert decode(lib, d, max_seq_len=4096, partition=512, ws=FAKE, wsb=n - 1) == WORKSPACE
     assert lib.chunked_prefill_paged_decode_workspace_size(d, 4096, 512) == n
+    # balanced split: prefix table plus two segment slots per worker (at least one work-group's worth)
+    s = lib.paged_gqa_decode_workspace_size(d, 4096, 0)
+    assert s >= 4 * 2 * 4 * (128 + 1) * 4 and s % 256 == 0
+    assert decode(lib, d, max_seq_len=4096, partition=0) == WORKSPACE
+    assert decode(lib, d, max_seq_len=4096, partition=0, ws=FAKE, wsb=256) == WORKSPACE
 
 
 def test_empty_batches_return_ok_without_launch(lib):

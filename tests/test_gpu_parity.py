@@ -155,6 +155,20 @@ def test_split_invariance():
         assert np.max(np.abs(o - outs[0])) <= 1e-5
 
 
+def test_workspace_reuse_across_shapes():
+    """One workspace (never cleared) serves decodes of different shapes and split modes in turn."""
+    a = wl.llama31_8b_decode(seed=13, num_seqs=9, ctx_lo=300, ctx_hi=2000)
+    b = wl.llama2_7b_sweep(1, seed=14, num_seqs=40)
+    c = wl.make_batch(name="c", seed=15, num_heads=16, num_kv_heads=2, head_dim=64, block_size=16,
+                      seq_lens=[700, 33, 1500], query_lens=[1, 1, 1], dtype=wl.F32)
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
+    for bt, P in ((a, 128), (b, 0), (c, 96), (a, 0), (b, 32), (c, 0), (a, 256)):
+        dev = DeviceBatch(bt)
+        ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
+                         bt.scale)
+        assert_parity(host(dev.decode(P, workspace=ws)), ref, bt.dtype, f"{bt.describe()} P={P}")
+
+
 # --------------------------------------------------------------------------
 # split-K reduce on its own
 # --------------------------------------------------------------------------
