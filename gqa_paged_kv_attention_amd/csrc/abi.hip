@@ -326,14 +326,16 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
     p.max_blocks_per_seq = dims.max_blocks_per_seq;
     p.num_tokens = num_tokens;
     p.scale_log2 = scale * 1.4426950408889634f;
-    const long long rpg = gqa::prefill_rows_per_group();
+    const bool kv_f32 = dims.kv_dtype == GQA_F32;
+    const long long rpg = kv_f32 ? gqa::prefill_rows_per_group() : gqa::prefill_lds_rows_per_group();
     // Upper bound on row tiles: every prefill sequence wastes at most one partial tile.
     const long long prefill_seqs = std::min<long long>(dims.num_seqs, num_tokens / 2);
     const long long tiles = ((long long)num_tokens * p.group + rpg - 1) / rpg + prefill_seqs;
     const long long groups = tiles * dims.num_kv_heads;
     if (groups > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-    hipError_t e = gqa::launch_prefill(p, dims.head_dim, dims.kv_dtype == GQA_F32, dims.out_dtype == GQA_F32,
-                                       (int)groups, s);
+    const bool out_f32 = dims.out_dtype == GQA_F32;
+    hipError_t e = kv_f32 ? gqa::launch_prefill(p, dims.head_dim, true, out_f32, (int)groups, s)
+                          : gqa::launch_prefill_lds(p, dims.head_dim, out_f32, (int)groups, s);
     if (e != hipSuccess) return GQA_ERR_LAUNCH;
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,

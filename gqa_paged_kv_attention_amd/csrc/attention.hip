@@ -490,42 +490,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int kv = blockIdx.x % a.num_kv_heads;
   const int tile = blockIdx.x / a.num_kv_heads;
 
-  // Locate (sequence, row tile) for this work-group: scan the per-sequence
-  // tile counts in chunks of kThreads sequences.
   __shared__ int s_scan[kThreads];
   __shared__ int s_found[2];
-  if (threadIdx.x == 0) s_found[0] = -1;
-  int base = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += kThreads) {
-    const int bb = c0 + threadIdx.x;
-    int cnt = 0;
-    if (bb < a.num_seqs) {
-      const int ql = a.query_start_loc[bb + 1] - a.query_start_loc[bb];
-      cnt = (ql > 1) ? (ql * G + RWG - 1) / RWG : 0;
-    }
-    s_scan[threadIdx.x] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = (threadIdx.x >= off) ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += add;
-      __syncthreads();
-    }
-    const int total = s_scan[kThreads - 1];
-    if (tile < base + total) {
-      const int incl = base + s_scan[threadIdx.x];
-      if (cnt > 0 && tile < incl && tile >= incl - cnt) {
-        s_found[0] = bb;
-        s_found[1] = tile - (incl - cnt);
-      }
-      __syncthreads();
-      break;
-    }
-    base += total;
-    __syncthreads();
-  }
-  __syncthreads();
-  const int b = s_found[0];
+  int local = 0;
+  const int b = locate_prefill_tile(a.query_start_loc, a.num_seqs, G, RWG, tile, s_scan, s_found, &local);
   if (b < 0) return;
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
@@ -537,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int rows_total = q_len * G;
   const int n_row_tiles = (rows_total + RWG - 1) / RWG;
   // heaviest row tile (most keys) of the sequence first
-  const int rt = n_row_tiles - 1 - s_found[1];
+  const int rt = n_row_tiles - 1 - local;
 
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, q = lane >> 4;

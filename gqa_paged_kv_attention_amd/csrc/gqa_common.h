@@ -60,6 +60,26 @@ __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_f16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Two bf16 (packed in a word) -> two fp16 (packed), rounding toward zero: exact
+// for values representable in fp16; larger magnitudes saturate at 65504.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x << 16),
+                                                                 __uint_as_float(x & 0xffff0000u)));
+}
+
+// Two fp32 -> two fp16 (packed), round to nearest even.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -68,17 +88,24 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max across the four lane groups that share a row (lanes n, n+16, n+32, n+48).
+// Max / sum across the four lane groups that share a row (lanes n, n+16,
+// n+32, n+48).  v_permlane16_swap(x, x) returns, in its two results, x of this
+// lane and of lane ^ 16 (in some order); v_permlane32_swap likewise for lane ^
+// 32.  Both are VALU operations, so the reduction stays off the LDS pipe.
 __device__ __forceinline__ float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float x0 = __uint_as_float(a[0]), x1 = __uint_as_float(a[1]);
+  x = x0 > x1 ? x0 : x1;
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y0 = __uint_as_float(b[0]), y1 = __uint_as_float(b[1]);
+  return y0 > y1 ? y0 : y1;
 }
 
 __device__ __forceinline__ float row_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Page id through the block table, clamped into the pool so that a corrupt
@@ -298,6 +325,49 @@ struct TileF32 {
     }
   }
 };
+
+// Locate this work-group's (sequence, row tile) among the row tiles of the
+// sequences with more than one query token (ceil(q_len * G / rows_per_group)
+// tiles each, in sequence order): a block-wide scan of the tile counts, in
+// chunks of blockDim.x sequences.  s_scan holds blockDim.x ints.  Returns the
+// sequence (or -1 past the last tile) and the tile's index within it.
+__device__ __forceinline__ int locate_prefill_tile(const int32_t* qsl, int num_seqs, int G, int rows_per_group,
+                                                   int tile, int* s_scan, int* s_found, int* local_tile) {
+  const int nthr = blockDim.x;
+  if (threadIdx.x == 0) s_found[0] = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += nthr) {
+    const int bb = c0 + threadIdx.x;
+    int cnt = 0;
+    if (bb < num_seqs) {
+      const int ql = qsl[bb + 1] - qsl[bb];
+      cnt = (ql > 1) ? (ql * G + rows_per_group - 1) / rows_per_group : 0;
+    }
+    s_scan[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < nthr; off <<= 1) {
+      const int add = (threadIdx.x >= off) ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const int total = s_scan[nthr - 1];
+    if (tile < base + total) {
+      const int incl = base + s_scan[threadIdx.x];
+      if (cnt > 0 && tile < incl && tile >= incl - cnt) {
+        s_found[0] = bb;
+        s_found[1] = tile - (incl - cnt);
+      }
+      __syncthreads();
+      break;
+    }
+    base += total;
+    __syncthreads();
+  }
+  __syncthreads();
+  *local_tile = s_found[1];
+  return s_found[0];
+}
 
 // Store 4 consecutive output channels (fp32 values) as fp32 or bf16.
 __device__ __forceinline__ void store4(float* dst, f32x4_t x) {

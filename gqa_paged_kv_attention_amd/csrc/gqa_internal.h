@@ -115,6 +115,9 @@ hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32,
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,
                           hipStream_t stream);
+// bf16 prefill with K/V tiles shared through LDS.
+int prefill_lds_rows_per_group();
+hipError_t launch_prefill_lds(const PrefillArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream);
 

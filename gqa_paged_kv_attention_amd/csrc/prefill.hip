@@ -1,0 +1,317 @@
+// Chunked prefill over the paged cache, bf16, with K/V tiles shared in LDS.
+//
+// The mixed batch of "[Kernel] [V1] Further optimizations to ROCm (Triton)
+// Backend to better handle GQA" (vLLM PR #14431, review thread on
+// chunked_prefill_paged_decode) runs a prefill kernel over the sequences with
+// more than one new token; each new token attends causally to the cached prefix
+// and to the chunk's earlier tokens (bottom-right aligned).
+//
+// GQA packing: the rows of a (sequence, kv head) are the pairs (new token j,
+// query head g of the group), r = j * G + g, so the G heads that share a kv
+// head share every K/V tile that is loaded ("[Performance] Use optimized
+// kernels for MQA/GQA", opening post: GQA should cut KV reads and let the dot
+// products run on matrix cores).  A work-group owns 4 waves x NTW blocks of 16
+// rows; the four waves load each 32-key tile once, cooperatively, into LDS
+// (double-buffered, the next tile's global loads in flight while the current
+// one is consumed) and each wave multiplies it against its own rows:
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 out),
+//   O^T += V^T P^T on v_mfma_f32_16x16x32_f16 with P rounded to fp16 (11-bit
+//   significand, relative error 2^-12) and V converted bf16 -> fp16 when the
+//   tile is written to LDS (exact for |v| in fp16's range; larger magnitudes
+//   saturate at 65504, a precondition of this path).
+#include "gqa_common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLazyRescale = 8.f;      // log2 growth of a row max before O is rescaled
+
+template <int D, int NTW>
+struct PrefillLds {
+  static constexpr int kRowsPerWave = NTW * 16;
+  static constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+  static constexpr int KC = D / 32;                 // 16-byte chunks of a row per Q.K^T product
+  static constexpr int DT = D / 16;                 // 16-channel output blocks
+  static constexpr int KROW = D + 8;                // LDS row stride of the key tile (elements)
+  static constexpr int VROW = kTile + 8;            // LDS row stride of the value tile (elements)
+  static constexpr int KCH = kTile * D / 8 / kThreads;   // 16-byte key chunks per thread per tile
+  static constexpr int VCH = 2 * D * 2 / kThreads;       // 16-byte value chunks per thread per tile
+};
+
+// LDS row of key token t.  A 128-bit LDS read is served 8 lanes at a time over
+// 32 four-byte banks, so with a 272-byte row stride row r lands in 16-byte bank
+// group r mod 8.  Lanes 0-7 of a Q.K^T product read tokens {0-3, 8-11} (+4, +16
+// for lanes 8-15): flipping bit 2 of tokens whose bit 3 is set sends those runs
+// to distinct groups.
+__device__ __forceinline__ int key_row(int t) { return t ^ ((t >> 1) & 4); }
+
+// max without the NaN canonicalisation fmaxf implies (operands are never NaN
+// here: masked scores are -inf, not NaN)
+__device__ __forceinline__ float max2(float a, float b) { return a > b ? a : b; }
+
+// This thread's share of a tile: for each 16-byte chunk, the page it comes from
+// (0 = first page of the tile, 1 = second), its element offset inside that
+// page, and its element offset in the LDS tile.
+template <int D, int NTW>
+struct TileCopyPlan {
+  typedef PrefillLds<D, NTW> S;
+  int k_page[S::KCH], k_src[S::KCH], k_dst[S::KCH];
+  int v_page[S::VCH], v_src[S::VCH], v_dst[S::VCH], v_tok[S::VCH];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < S::KCH; ++i) {
+      const int ci = threadIdx.x + i * kThreads;
+      const int token = ci / (D / 8), col = ci % (D / 8);
+      k_page[i] = token / kPage;
+      k_src[i] = (token % kPage) * D + col * 8;
+      k_dst[i] = key_row(token) * S::KROW + col * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < S::VCH; ++i) {
+      const int ci = threadIdx.x + i * kThreads;
+      const int h = ci / (2 * D), rem = ci % (2 * D);
+      const int d = rem / 2, e = rem % 2;
+      v_page[i] = h;
+      v_src[i] = d * kPage + 8 * e;
+      v_dst[i] = d * S::VROW + 16 * h + 8 * e;
+      v_tok[i] = 16 * h + 8 * e;                     // first token (in the tile) of this 8-token run
+    }
+  }
+};
+
+template <int D, int NTW>
+__device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW>& plan,
+                                               const uint16_t* kA, const uint16_t* kB, const uint16_t* vA,
+                                               const uint16_t* vB) {
+  typedef PrefillLds<D, NTW> S;
+#pragma unroll
+  for (int i = 0; i < S::KCH; ++i) kreg[i] = ld16((plan.k_page[i] ? kB : kA) + plan.k_src[i]);
+#pragma unroll
+  for (int i = 0; i < S::VCH; ++i) vreg[i] = ld16((plan.v_page[i] ? vB : vA) + plan.v_src[i]);
+}
+
+// Registers -> LDS; values are converted to fp16, and with `tail` set those of
+// tokens at or past L become 0.
+template <int D, int NTW>
+__device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const uint4* kreg, const uint4* vreg,
+                                               const TileCopyPlan<D, NTW>& plan, int tile_base, int L, bool tail) {
+  typedef PrefillLds<D, NTW> S;
+#pragma unroll
+  for (int i = 0; i < S::KCH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
+#pragma unroll
+  for (int i = 0; i < S::VCH; ++i) {
+    uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+    if (tail) {
+      const int t0 = tile_base + plan.v_tok[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] &= (t0 + 2 * k < L ? 0xFFFFu : 0u) | (t0 + 2 * k + 1 < L ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = bf16x2_to_f16x2(w[k]);
+    *reinterpret_cast<uint4*>(sV + plan.v_dst[i]) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int D, int NTW, class OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NTW <= 2 ? 2 : 1)))
+void prefill_lds_kernel(PrefillArgs a) {
+  typedef PrefillLds<D, NTW> S;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * S::KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * S::VROW];
+  __shared__ int s_scan[kThreads];
+  __shared__ int s_found[2];
+
+  const int G = a.group;
+  const int kv = blockIdx.x % a.num_kv_heads;
+  const int tile = blockIdx.x / a.num_kv_heads;
+  int local = 0;
+  const int b = uniform(
+      locate_prefill_tile(a.query_start_loc, a.num_seqs, G, S::kRowsPerGroup, tile, s_scan, s_found, &local));
+  local = uniform(local);
+  if (b < 0) return;
+  const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+  const int q_len = q1 - q0;
+  if (q1 > a.num_tokens || q0 < 0) return;
+  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
+  const int prior = L - q_len;
+  if (prior < 0) return;
+  const int rows_total = q_len * G;
+  const int n_row_tiles = (rows_total + S::kRowsPerGroup - 1) / S::kRowsPerGroup;
+  const int rt = n_row_tiles - 1 - local;        // heaviest row tile of the sequence first
+
+  const int lane = lane_id(), w = wave_id();
+  const int n = lane & 15, q = lane >> 4;
+  const int r0 = rt * S::kRowsPerGroup + w * S::kRowsPerWave;
+  const bool wave_rows = r0 < rows_total;
+
+  uint4 qf[NTW][S::KC];
+  int lim[NTW], tok[NTW], head[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int r = r0 + nt * 16 + n;
+    const bool valid = r < rows_total;
+    const int j = r / G, g = r % G;
+    lim[nt] = valid ? prior + j : -1;
+    tok[nt] = valid ? q0 + j : -1;
+    head[nt] = kv * G + g;
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.query) + ((size_t)(valid ? tok[nt] : 0) * a.num_heads + head[nt]) * D;
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c) qf[nt][c] = valid ? ld16(qrow + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+  }
+  const int lim_lo = prior + r0 / G;
+  const int lim_hi = wave_rows ? prior + min(q_len - 1, (r0 + S::kRowsPerWave - 1) / G) : -1;
+  const int group_hi = prior + min(q_len - 1, (rt * S::kRowsPerGroup + S::kRowsPerGroup - 1) / G);
+  const int n_tiles = group_hi / kTile + 1;
+  const int npages = (L + kPage - 1) / kPage;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache);
+  const size_t head_off = (size_t)kv * (kPage * D);
+  const size_t page_stride = (size_t)a.num_kv_heads * (kPage * D);
+
+  TileCopyPlan<D, NTW> plan;
+  plan.init();
+  // the two pages of tile t (t clamped to the last tile), as wave-uniform ids
+  auto tile_pages = [&](int t, int& pA, int& pB) {
+    const int pg = min(t, n_tiles - 1) * 2;
+    pA = uniform(page_at(bt, pg, a.num_blocks));
+    pB = uniform(page_at(bt, min(pg + 1, npages - 1), a.num_blocks));
+  };
+  auto issue = [&](int pA, int pB, uint4* kr, uint4* vr) {
+    load_tile_regs<D, NTW>(kr, vr, plan, kc + pA * page_stride + head_off, kc + pB * page_stride + head_off,
+                           vc + pA * page_stride + head_off, vc + pB * page_stride + head_off);
+  };
+
+  float m[NTW], l[NTW];
+  f32x4_t o[NTW][S::DT];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] = zero4();
+  }
+
+  uint4 kreg[S::KCH], vreg[S::VCH];
+  int pA, pB;
+  tile_pages(0, pA, pB);
+  issue(pA, pB, kreg, vreg);
+  store_tile_lds<D, NTW>(sK[0], sV[0], kreg, vreg, plan, 0, L, kTile > L);
+  tile_pages(1, pA, pB);
+  __syncthreads();
+
+  // LDS offsets of this lane's key rows (products s = 0, 1; token fed to row m
+  // as in TileBF16) and value rows
+  const int kslot = ((n < 8) ? 0 : kPage) + (n & 3) + 8 * ((n >> 2) & 1);
+  const int koff0 = key_row(kslot) * S::KROW + 8 * q, koff1 = key_row(kslot + 4) * S::KROW + 8 * q;
+  const int voff = n * S::VROW + 8 * q;
+
+  // One tile against this wave's rows; `masked` applies the causal limit per
+  // score (tiles wholly below the diagonal skip it).
+  auto compute = [&](const uint16_t* K, const uint16_t* V, int tb, bool masked) {
+    f32x4_t acc[NTW][2];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int c = 0; c < S::KC; ++c) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(K + (s ? koff1 : koff0) + 32 * c);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[nt][s] = mfma_bf16(kf, qf[nt][c], acc[nt][s]);
+      }
+    }
+    uint4 pf[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float sc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sc[i] = i < 4 ? acc[nt][0][i] : acc[nt][1][i - 4];
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = (tb + 8 * q + i <= lim[nt]) ? sc[i] : -INFINITY;
+      }
+      float mx = max2(max2(max2(sc[0], sc[1]), max2(sc[2], sc[3])), max2(max2(sc[4], sc[5]), max2(sc[6], sc[7])));
+      // running max in log2 units; raised (and O, l rescaled) only when some
+      // row's max grows by more than kLazyRescale, so P stays <= 2^kLazyRescale
+      const float cand = row_max4(mx) * a.scale_log2;
+      if (__any(cand > m[nt] + kLazyRescale)) {
+        const float m_new = max2(m[nt], cand);
+        const float alpha = fast_exp2(m[nt] - (m_new == -INFINITY ? 0.f : m_new));
+        l[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] *= alpha;
+        m[nt] = m_new;
+      }
+      const float m_use = (m[nt] == -INFINITY) ? 0.f : m[nt];
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sc[i] = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -m_use));
+        rs += sc[i];
+      }
+      l[nt] += rs;
+      pf[nt] = make_uint4(f32x2_to_f16x2(sc[0], sc[1]), f32x2_to_f16x2(sc[2], sc[3]), f32x2_to_f16x2(sc[4], sc[5]),
+                          f32x2_to_f16x2(sc[6], sc[7]));
+    }
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+      const uint4 vf = *reinterpret_cast<const uint4*>(V + voff + 16 * dt * S::VROW);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) o[nt][dt] = mfma_f16(vf, pf[nt], o[nt][dt]);
+    }
+  };
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const int tb = it * kTile;
+    const bool more = it + 1 < n_tiles;
+    // tile it + 1: global loads in flight while tile it is computed
+    if (more) issue(pA, pB, kreg, vreg);
+    tile_pages(it + 2, pA, pB);
+    if (tb <= lim_hi) compute(sK[buf], sV[buf], tb, tb + kTile - 1 > lim_lo);
+    if (more) store_tile_lds<D, NTW>(sK[buf ^ 1], sV[buf ^ 1], kreg, vreg, plan, tb + kTile, L, tb + 2 * kTile > L);
+    __syncthreads();
+  }
+
+  if (!wave_rows) return;
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float lr = row_sum4(l[nt]);
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    if (tok[nt] >= 0) {
+      OutT* dst = out + ((size_t)tok[nt] * a.num_heads + head[nt]) * D + 4 * q;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) store4(dst + dt * 16, o[nt][dt] * inv);
+    }
+  }
+}
+
+constexpr int kLdsNTW = 2;
+
+template <class OutT>
+hipError_t dispatch(const PrefillArgs& a, int D, int groups, hipStream_t s) {
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_lds_kernel<64, kLdsNTW, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_lds_kernel<128, kLdsNTW, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_lds_rows_per_group() { return PrefillLds<128, kLdsNTW>::kRowsPerGroup; }
+
+hipError_t launch_prefill_lds(const PrefillArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream) {
+  return out_f32 ? dispatch<float>(a, head_dim, grid_groups, stream)
+                 : dispatch<uint16_t>(a, head_dim, grid_groups, stream);
+}
+
+}  // namespace gqa
