@@ -3,7 +3,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "../../include/gqa_paged.h"
+#include "gqa_paged.h"
 #include "gqa_internal.h"
 
 namespace {

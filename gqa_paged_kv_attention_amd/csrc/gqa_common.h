@@ -74,11 +74,25 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
                                                                  __uint_as_float(x & 0xffff0000u)));
 }
 
-// Two fp32 -> two fp16 (packed), round to nearest even.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two fp16 (packed), round to nearest even (one v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
 }
+
+// A value the optimiser cannot see through (the empty asm emits nothing).
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// max(a, b) for non-NaN operands as one v_med3_f32(a, b, pinf), pinf = +inf
+// made opaque: with a literal +inf the optimiser turns it back into fmaxf,
+// which quiets NaNs first (an extra v_max_f32 per operand whose origin it
+// cannot trace).
+__device__ __forceinline__ float fmax_nn(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
 
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -19,6 +19,8 @@
 //   significand, relative error 2^-12) and V converted bf16 -> fp16 when the
 //   tile is written to LDS (exact for |v| in fp16's range; larger magnitudes
 //   saturate at 65504, a precondition of this path).
+// The softmax denominator is the same product with V replaced by ones, so it
+// sums exactly the rounded P that weighs V and costs no VALU additions.
 #include "gqa_common.h"
 #include "gqa_internal.h"
 
@@ -59,6 +61,8 @@ __device__ __forceinline__ float max2(float a, float b) { return a > b ? a : b; 
 template <int D, int NTW>
 struct TileCopyPlan {
   typedef PrefillLds<D, NTW> S;
+  // k_page / v_page are wave-uniform: 16 tokens of keys (or 16 tokens of one
+  // page's values) are a multiple of a wave's 64 chunks for D = 64 and 128
   int k_page[S::KCH], k_src[S::KCH], k_dst[S::KCH];
   int v_page[S::VCH], v_src[S::VCH], v_dst[S::VCH], v_tok[S::VCH];
   __device__ __forceinline__ void init() {
@@ -66,7 +70,7 @@ struct TileCopyPlan {
     for (int i = 0; i < S::KCH; ++i) {
       const int ci = threadIdx.x + i * kThreads;
       const int token = ci / (D / 8), col = ci % (D / 8);
-      k_page[i] = token / kPage;
+      k_page[i] = uniform(token / kPage);
       k_src[i] = (token % kPage) * D + col * 8;
       k_dst[i] = key_row(token) * S::KROW + col * 8;
     }
@@ -75,7 +79,7 @@ struct TileCopyPlan {
       const int ci = threadIdx.x + i * kThreads;
       const int h = ci / (2 * D), rem = ci % (2 * D);
       const int d = rem / 2, e = rem % 2;
-      v_page[i] = h;
+      v_page[i] = uniform(h);
       v_src[i] = d * kPage + 8 * e;
       v_dst[i] = d * S::VROW + 16 * h + 8 * e;
       v_tok[i] = 16 * h + 8 * e;                     // first token (in the tile) of this 8-token run
@@ -149,6 +153,14 @@ void prefill_lds_kernel(PrefillArgs a) {
   const int r0 = rt * S::kRowsPerGroup + w * S::kRowsPerWave;
   const bool wave_rows = r0 < rows_total;
 
+  // Scores are scaled after their max is taken, which needs a positive scale:
+  // a negative one flips the query's sign (exact in bf16) and |scale| is used;
+  // a zero scale (every visible score 0) zeroes the query and uses 1, so that
+  // masked scores stay -inf instead of -inf * 0.
+  const bool zero_scale = a.scale_log2 == 0.f;
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const uint32_t qkeep = zero_scale ? 0u : 0xFFFFFFFFu;
+  const float sl2 = zero_scale ? 1.f : __builtin_fabsf(a.scale_log2);
   uint4 qf[NTW][S::KC];
   int lim[NTW], tok[NTW], head[NTW];
 #pragma unroll
@@ -162,7 +174,14 @@ void prefill_lds_kernel(PrefillArgs a) {
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(a.query) + ((size_t)(valid ? tok[nt] : 0) * a.num_heads + head[nt]) * D;
 #pragma unroll
-    for (int c = 0; c < S::KC; ++c) qf[nt][c] = valid ? ld16(qrow + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < S::KC; ++c) {
+      uint4 x = valid ? ld16(qrow + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+      x.x = (x.x ^ qsign) & qkeep;
+      x.y = (x.y ^ qsign) & qkeep;
+      x.z = (x.z ^ qsign) & qkeep;
+      x.w = (x.w ^ qsign) & qkeep;
+      qf[nt][c] = x;
+    }
   }
   const int lim_lo = prior + r0 / G;
   const int lim_hi = wave_rows ? prior + min(q_len - 1, (r0 + S::kRowsPerWave - 1) / G) : -1;
@@ -170,40 +189,43 @@ void prefill_lds_kernel(PrefillArgs a) {
   const int n_tiles = group_hi / kTile + 1;
   const int npages = (L + kPage - 1) / kPage;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache);
-  const size_t head_off = (size_t)kv * (kPage * D);
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache) + (size_t)kv * (kPage * D);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache) + (size_t)kv * (kPage * D);
   const size_t page_stride = (size_t)a.num_kv_heads * (kPage * D);
 
   TileCopyPlan<D, NTW> plan;
   plan.init();
-  // the two pages of tile t (t clamped to the last tile), as wave-uniform ids
-  auto tile_pages = [&](int t, int& pA, int& pB) {
+  // Raw block-table entries of tile t (clamped to the last tile).  They are
+  // loaded one iteration before they are used, so that waiting for them never
+  // waits for the K/V loads issued just before.
+  auto fetch_pages = [&](int t, int& rawA, int& rawB) {
     const int pg = min(t, n_tiles - 1) * 2;
-    pA = uniform(page_at(bt, pg, a.num_blocks));
-    pB = uniform(page_at(bt, min(pg + 1, npages - 1), a.num_blocks));
+    rawA = bt[pg];
+    rawB = bt[min(pg + 1, npages - 1)];
   };
+  auto page_id = [&](int raw) { return uniform((unsigned)raw < (unsigned)a.num_blocks ? raw : 0); };
   auto issue = [&](int pA, int pB, uint4* kr, uint4* vr) {
-    load_tile_regs<D, NTW>(kr, vr, plan, kc + pA * page_stride + head_off, kc + pB * page_stride + head_off,
-                           vc + pA * page_stride + head_off, vc + pB * page_stride + head_off);
+    load_tile_regs<D, NTW>(kr, vr, plan, kc + pA * page_stride, kc + pB * page_stride, vc + pA * page_stride,
+                           vc + pB * page_stride);
   };
 
-  float m[NTW], l[NTW];
-  f32x4_t o[NTW][S::DT];
+  float m[NTW], mu[NTW];
+  f32x4_t o[NTW][S::DT], ol[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     m[nt] = -INFINITY;
-    l[nt] = 0.f;
+    mu[nt] = 0.f;
+    ol[nt] = zero4();
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] = zero4();
   }
 
   uint4 kreg[S::KCH], vreg[S::VCH];
-  int pA, pB;
-  tile_pages(0, pA, pB);
-  issue(pA, pB, kreg, vreg);
+  int rawA, rawB;
+  fetch_pages(0, rawA, rawB);
+  issue(page_id(rawA), page_id(rawB), kreg, vreg);
   store_tile_lds<D, NTW>(sK[0], sV[0], kreg, vreg, plan, 0, L, kTile > L);
-  tile_pages(1, pA, pB);
+  fetch_pages(1, rawA, rawB);
   __syncthreads();
 
   // LDS offsets of this lane's key rows (products s = 0, 1; token fed to row m
@@ -211,6 +233,8 @@ void prefill_lds_kernel(PrefillArgs a) {
   const int kslot = ((n < 8) ? 0 : kPage) + (n & 3) + 8 * ((n >> 2) & 1);
   const int koff0 = key_row(kslot) * S::KROW + 8 * q, koff1 = key_row(kslot + 4) * S::KROW + 8 * q;
   const int voff = n * S::VROW + 8 * q;
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0 x 8
+  const float pinf = opaque(INFINITY);
 
   // One tile against this wave's rows; `masked` applies the causal limit per
   // score (tiles wholly below the diagonal skip it).
@@ -219,12 +243,13 @@ void prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero4();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int c = 0; c < S::KC; ++c) {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(K + koff0 + 32 * c);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(K + koff1 + 32 * c);
 #pragma unroll
-      for (int c = 0; c < S::KC; ++c) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(K + (s ? koff1 : koff0) + 32 * c);
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[nt][s] = mfma_bf16(kf, qf[nt][c], acc[nt][s]);
+      for (int nt = 0; nt < NTW; ++nt) {
+        acc[nt][0] = mfma_bf16(k0, qf[nt][c], acc[nt][0]);
+        acc[nt][1] = mfma_bf16(k1, qf[nt][c], acc[nt][1]);
       }
     }
     uint4 pf[NTW];
@@ -237,28 +262,27 @@ void prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) sc[i] = (tb + 8 * q + i <= lim[nt]) ? sc[i] : -INFINITY;
       }
-      float mx = max2(max2(max2(sc[0], sc[1]), max2(sc[2], sc[3])), max2(max2(sc[4], sc[5]), max2(sc[6], sc[7])));
-      // running max in log2 units; raised (and O, l rescaled) only when some
-      // row's max grows by more than kLazyRescale, so P stays <= 2^kLazyRescale
-      const float cand = row_max4(mx) * a.scale_log2;
-      if (__any(cand > m[nt] + kLazyRescale)) {
-        const float m_new = max2(m[nt], cand);
-        const float alpha = fast_exp2(m[nt] - (m_new == -INFINITY ? 0.f : m_new));
-        l[nt] *= alpha;
+      const float mx = fmax_nn(fmax_nn(fmax_nn(sc[0], sc[1], pinf), fmax_nn(sc[2], sc[3], pinf), pinf),
+                               fmax_nn(fmax_nn(sc[4], sc[5], pinf), fmax_nn(sc[6], sc[7], pinf), pinf), pinf);
+      // Running max in log2 units, raised (and O rescaled) only when some row's
+      // max grows by more than kLazyRescale, so P stays <= 2^kLazyRescale.  A
+      // lane's own max decides whether any row needs it; only then is the row
+      // max taken across the row's four lanes.
+      if (__any(mx * sl2 > m[nt] + kLazyRescale)) {
+        const float m_new = fmax_nn(m[nt], row_max4(mx) * sl2, pinf);
+        const float mu_new = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m[nt] - mu_new);     // 0 while m = -inf (O and l are 0)
+        ol[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] *= alpha;
         m[nt] = m_new;
+        mu[nt] = mu_new;
       }
-      const float m_use = (m[nt] == -INFINITY) ? 0.f : m[nt];
-      float rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sc[i] = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -m_use));
-        rs += sc[i];
-      }
-      l[nt] += rs;
+      for (int i = 0; i < 8; ++i) sc[i] = fast_exp2(__builtin_fmaf(sc[i], sl2, -mu[nt]));
       pf[nt] = make_uint4(f32x2_to_f16x2(sc[0], sc[1]), f32x2_to_f16x2(sc[2], sc[3]), f32x2_to_f16x2(sc[4], sc[5]),
                           f32x2_to_f16x2(sc[6], sc[7]));
+      ol[nt] = mfma_f16(ones, pf[nt], ol[nt]);
     }
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
@@ -272,9 +296,11 @@ void prefill_lds_kernel(PrefillArgs a) {
     const int buf = it & 1;
     const int tb = it * kTile;
     const bool more = it + 1 < n_tiles;
-    // tile it + 1: global loads in flight while tile it is computed
+    // tile it + 1: global loads in flight while tile it is computed; the
+    // block-table entries of tile it + 2 follow them
+    const int pA = page_id(rawA), pB = page_id(rawB);
     if (more) issue(pA, pB, kreg, vreg);
-    tile_pages(it + 2, pA, pB);
+    fetch_pages(it + 2, rawA, rawB);
     if (tb <= lim_hi) compute(sK[buf], sV[buf], tb, tb + kTile - 1 > lim_lo);
     if (more) store_tile_lds<D, NTW>(sK[buf ^ 1], sV[buf ^ 1], kreg, vreg, plan, tb + kTile, L, tb + 2 * kTile > L);
     __syncthreads();
@@ -284,7 +310,8 @@ void prefill_lds_kernel(PrefillArgs a) {
   OutT* out = reinterpret_cast<OutT*>(a.out);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    const float lr = row_sum4(l[nt]);
+    // every element of ol is the row sum of the rounded P of this lane's row
+    const float lr = ol[nt][0];
     const float inv = lr > 0.f ? 1.f / lr : 0.f;
     if (tok[nt] >= 0) {
       OutT* dst = out + ((size_t)tok[nt] * a.num_heads + head[nt]) * D + 4 * q;

@@ -238,6 +238,24 @@ def test_mixed_edge_shapes(dtype, d, hq, hkv):
         assert_parity(host(dev.mixed(partition)), ref, dtype, f"{bt.describe()} P={partition}")
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.3])
+def test_mixed_scale_sign(dtype, scale):
+    """The softmax is of scale * q.k for any finite scale: a negative scale
+    reverses which keys dominate, zero averages the visible values."""
+    q_lens = [1, 40, 3, 1, 97]
+    prior = [50, 0, 200, 7, 33]
+    bt = wl.make_batch(name="scale", seed=41, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                       seq_lens=[a + b for a, b in zip(q_lens, prior)], query_lens=q_lens, dtype=dtype)
+    dev = DeviceBatch(bt)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, scale)
+    got = host(ops.chunked_prefill_paged_decode(dev.query, dev.key_cache, dev.value_cache, dev.block_tables,
+                                                dev.seq_lens, dev.query_start_loc, bt.max_query_len, bt.max_seq_len,
+                                                scale))
+    assert_parity(got, ref, dtype, f"{bt.describe()} scale={scale}")
+
+
 def test_prefill_chunk_invariance_on_gpu():
     """A 96-token chunk equals three sequential 32-token chunks over the same cache."""
     L, C = 400, 96
