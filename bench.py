@@ -159,7 +159,7 @@ def main():
         mout = torch.empty(mb.num_tokens, mb.num_heads, mb.head_dim, dtype=torch.float32, device=dev)
         mdims = ops.make_dims(num_seqs=mb.num_seqs, num_heads=mb.num_heads, key_cache=mkc, block_tables=mt,
                               q_dtype=mq.dtype, out_dtype=mout.dtype)
-        mws = torch.zeros(max(ops.decode_workspace_size(mdims, mb.max_seq_len, args.mixed_partition), 1),
+        mws = torch.zeros(max(ops.mixed_workspace_size(mdims, mb.num_tokens, mb.max_seq_len, args.mixed_partition), 1),
                           dtype=torch.uint8, device=dev)
         ops.reshape_and_cache(mnk, mnv, mkc, mvc, mt, ml, mqsl)
 

@@ -1,289 +1,20 @@
 // Paged GQA attention kernels for gfx950: decode (fixed split-K partitions or
-// a balanced persistent split) and chunked prefill.
-//
-// All kernels read each (sequence, kv head) K/V page once per work item and
-// share it across the G query heads of the group, as "[Performance] Use
-// optimized kernels for MQA/GQA" (vLLM issue #1880, opening post) asks of a
-// GQA-aware kernel, instead of expanding K/V per query head.  The G heads (and
+// a balanced persistent split) and the fp32 chunked prefill.  The G heads (and
 // for prefill, the chunk's new tokens times G) form the 16-wide column block of
-// the matrix-core products described in gqa_common.h.
-#include "gqa_common.h"
-#include "gqa_internal.h"
+// the matrix-core products described in gqa_common.h; the per-wave tile
+// pipeline is in decode_core.h.
+#include "decode_core.h"
 
 namespace gqa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
-
-template <class T>
-__device__ __forceinline__ const T* page_ptr(const void* cache, int page, int num_kv_heads, int kv, int D) {
-  return reinterpret_cast<const T*>(cache) + ((size_t)page * num_kv_heads + kv) * (size_t)(kPage * D);
-}
-
-// One online-softmax + P.V step for a 16-row block.  `s` holds the block's 8
-// raw scores of this lane (tile-relative tokens Tile::token_offset(q, idx));
-// `lim` is the last visible key position of this lane's row (inclusive) and is
-// applied only when `masked`.
-template <class Tile>
-__device__ __forceinline__ void softmax_pv(float s[8], float& m, float& l, f32x4_t* o, const typename Tile::V& vf,
-                                           float scale_log2, bool masked, int tile_base, int lim, int q) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float x = s[i] * scale_log2;
-    if (masked) x = (tile_base + Tile::token_offset(q, i) <= lim) ? x : -INFINITY;
-    s[i] = x;
-    mx = fmaxf(mx, x);
-  }
-  mx = row_max4(mx);
-  const float m_new = fmaxf(m, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(m - m_use);
-  float rs = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s[i] = fast_exp2(s[i] - m_use);
-    rs += s[i];
-  }
-  l = l * alpha + rs;
-  m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < Tile::DT; ++dt) o[dt] *= alpha;
-  Tile::pv(o, vf, s);
-}
-
-// Running softmax state of one wave for NT blocks of 16 rows.
-template <class Tile, int NT>
-struct WaveState {
-  float m[NT], l[NT];
-  f32x4_t o[NT][Tile::DT];
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      m[nt] = -INFINITY;
-      l[nt] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < Tile::DT; ++dt) o[nt][dt] = zero4();
-    }
-  }
-};
-
-// Decode rows of one (sequence, kv head) for this wave: G heads in NT blocks.
-template <class Tile, int D, int NT>
-__device__ __forceinline__ void load_group_query(typename Tile::Q qf[NT], const void* query, int row, int num_heads,
-                                                 int kv, int G, int lane) {
-  typedef typename Tile::elem_t elem_t;
-  const int n = lane & 15;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int g = nt * 16 + n;
-    const elem_t* qrow =
-        (g < G) ? reinterpret_cast<const elem_t*>(query) + ((size_t)row * num_heads + kv * G + g) * D : nullptr;
-    Tile::load_q(qf[nt], qrow, lane);
-  }
-}
-
-// Walk tiles it0, it0+step, ... < it1 of one (sequence, kv head); tile i covers
-// keys [32 i, 32 i + 32).  Keys past `lim` are masked; values of tokens at or
-// past L are zeroed so that whatever sits in the pool beyond the sequence
-// (including NaN) cannot reach the output.
-//
-// Software pipelining: two register sets (A, B) alternate, and the loads of
-// the next tile are issued before the current tile is computed, so a wave
-// always has a tile in flight.  The prefetch is unconditional (its tile index
-// is clamped to the last tile, whose re-read hits in cache), which keeps the
-// load count per iteration fixed and lets the compiler wait on just the
-// current tile's loads.
-template <class Tile, int D>
-struct TilePages {
-  int pA, pB;
-  __device__ __forceinline__ void fetch(const int32_t* bt, int it, int npages, int num_blocks) {
-    const int pg = it * (kTile / kPage);
-    pA = page_at(bt, pg, num_blocks);
-    pB = page_at(bt, min(pg + 1, npages - 1), num_blocks);
-  }
-};
-
-template <class Tile, int D>
-__device__ __forceinline__ void load_tile(typename Tile::K& kf, typename Tile::V& vf, const TilePages<Tile, D>& pg,
-                                          const void* kc, const void* vc, int num_kv_heads, int kv, int lane) {
-  typedef typename Tile::elem_t elem_t;
-  Tile::load_k(kf, page_ptr<elem_t>(kc, pg.pA, num_kv_heads, kv, D), page_ptr<elem_t>(kc, pg.pB, num_kv_heads, kv, D),
-               lane);
-  Tile::load_v(vf, page_ptr<elem_t>(vc, pg.pA, num_kv_heads, kv, D), page_ptr<elem_t>(vc, pg.pB, num_kv_heads, kv, D),
-               lane);
-}
-
-template <class Tile, int NT>
-__device__ __forceinline__ void compute_tile(WaveState<Tile, NT>& st, const typename Tile::Q qf[NT],
-                                             const typename Tile::K& kf, typename Tile::V& vf, int tb, int L, int lim,
-                                             float scale_log2, int lane) {
-  const int q = lane >> 4;
-  const bool masked = tb + kTile - 1 > lim;
-  if (tb + kTile > L) Tile::mask_v(vf, tb, L, lane);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float s[8];
-    Tile::qk(s, kf, qf[nt]);
-    softmax_pv<Tile>(s, st.m[nt], st.l[nt], st.o[nt], vf, scale_log2, masked, tb, lim, q);
-  }
-}
-
-template <class Tile, int D, int NT>
-__device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typename Tile::Q qf[NT], const void* kc,
-                                          const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
-                                          int L, int lim, int it0, int it1, int step, float scale_log2, int lane) {
-  if (it0 >= it1) return;
-  const int npages = (L + kPage - 1) / kPage;
-  if constexpr (!Tile::kPipelined) {
-    for (int it = it0; it < it1; it += step) {
-      typename Tile::K kf;
-      typename Tile::V vf;
-      TilePages<Tile, D> pg;
-      pg.fetch(bt, it, npages, num_blocks);
-      load_tile<Tile, D>(kf, vf, pg, kc, vc, num_kv_heads, kv, lane);
-      compute_tile<Tile, NT>(st, qf, kf, vf, it * kTile, L, lim, scale_log2, lane);
-    }
-    return;
-  }
-  const int last = it0 + (it1 - 1 - it0) / step * step;     // last tile this wave visits
-  typename Tile::K kA, kB;
-  typename Tile::V vA, vB;
-  TilePages<Tile, D> pg;
-  pg.fetch(bt, it0, npages, num_blocks);
-  load_tile<Tile, D>(kA, vA, pg, kc, vc, num_kv_heads, kv, lane);
-  pg.fetch(bt, min(it0 + step, last), npages, num_blocks);
-  for (int it = it0;; it += 2 * step) {
-    // B <- tile it + step (clamped), then compute A = tile it
-    load_tile<Tile, D>(kB, vB, pg, kc, vc, num_kv_heads, kv, lane);
-    pg.fetch(bt, min(it + 2 * step, last), npages, num_blocks);
-    compute_tile<Tile, NT>(st, qf, kA, vA, it * kTile, L, lim, scale_log2, lane);
-    if (it + step > last) break;
-    // A <- tile it + 2 step (clamped), then compute B = tile it + step
-    load_tile<Tile, D>(kA, vA, pg, kc, vc, num_kv_heads, kv, lane);
-    pg.fetch(bt, min(it + 3 * step, last), npages, num_blocks);
-    compute_tile<Tile, NT>(st, qf, kB, vB, (it + step) * kTile, L, lim, scale_log2, lane);
-    if (it + 2 * step > last) break;
-  }
-}
-
-// Clamp a sequence length into what the block table can address.
-__device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq) {
-  return max(0, min(L, max_blocks_per_seq * kPage));
-}
-
-// ---------------------------------------------------------------------------
-// Fixed-partition decode: grid (max_partitions, Hkv, B), 4 waves.  Sequence b
-// is split into n = ceil(L / partition_size) partitions of nearly equal length
-// (whole 32-token tiles); the work-group owns partition p of one (sequence, kv
-// head), its waves take the partition's tiles round-robin and merge through
-// LDS.  With n == 1 the work-group writes `out`; otherwise it writes the
-// partition's normalised output and log-sum-exp for the split-K reduce kernel.
-// ---------------------------------------------------------------------------
-// Waves per SIMD the decode kernels are compiled for: two when a double-buffered
-// K/V tile (2 x 2 x 32 tokens x D x elem bytes per wave) fits next to one row
-// block's state, else one.
-template <class Tile, int D, int NT>
-constexpr int decode_waves_per_simd() {
-  return (NT == 1 && (sizeof(typename Tile::elem_t) * D <= 256 || !Tile::kPipelined)) ? 2 : 1;
-}
-
+// Fixed-partition decode: grid (max_partitions, Hkv, B).
 template <class Tile, int D, int NT, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void decode_kernel(DecodeArgs a) {
-  constexpr int R = NT * 16;            // padded rows of the group
-  const int p = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int G = a.group;
-  const int lane = lane_id(), w = wave_id();
-  const int n = lane & 15, q = lane >> 4;
-
-  int row = b;
-  if (a.query_start_loc) {
-    const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
-    if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
-    row = q0;
-  }
-  typename Tile::Q qf[NT];
-  load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
-
-  const int L = min(clamp_len(a.seq_lens[b], a.max_blocks_per_seq), a.max_partitions * a.partition_size);
-  const int nparts = (L + a.partition_size - 1) / a.partition_size;
-  OutT* out = reinterpret_cast<OutT*>(a.out);
-
-  if (L == 0) {
-    if (p == 0)
-      for (int i = threadIdx.x; i < G * D; i += kThreads)
-        store1(out + ((size_t)row * a.num_heads + kv * G) * D + i, 0.f);
-    return;
-  }
-  if (p >= nparts) return;
-
-  // equal split of the sequence's tiles over its partitions (each gets >= 1 tile)
-  const int tiles_all = (L + kTile - 1) / kTile;
-  const int per = tiles_all / nparts, extra = tiles_all % nparts;
-  const int tile0 = p * per + min(p, extra);
-  const int n_tiles = per + (p < extra ? 1 : 0);
-  const int t1 = min((tile0 + n_tiles) * kTile, L);
-
-  WaveState<Tile, NT> st;
-  st.reset();
-  run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                         a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0 + w, tile0 + n_tiles, kWaves,
-                         a.scale_log2, lane);
-
-  // ---- merge the four waves ----
-  __shared__ float sm_m[kWaves][R];
-  __shared__ float sm_l[kWaves][R];
-  __shared__ float sm_o[kWaves][R][D + 4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lr = row_sum4(st.l[nt]);
-    if (q == 0) {
-      sm_m[w][nt * 16 + n] = st.m[nt];
-      sm_l[w][nt * 16 + n] = lr;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + n;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][r]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float Ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
-    const float f = (Ls > 0.f) ? fast_exp2(st.m[nt] - Mu) / Ls : 0.f;
-    if (r < G) {
-#pragma unroll
-      for (int dt = 0; dt < Tile::DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm_o[w][r][dt * 16 + 4 * q + j] = st.o[nt][dt][j] * f;
-    }
-  }
-  __syncthreads();
-
-  const size_t head0 = (size_t)b * a.num_heads + kv * G;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int r = i / D, d = i % D;
-    const float v = sm_o[0][r][d] + sm_o[1][r][d] + sm_o[2][r][d] + sm_o[3][r][d];
-    if (nparts == 1)
-      store1(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
-    else
-      a.partial_out[((head0 + r) * a.max_partitions + p) * D + d] = v;
-  }
-  if (nparts > 1 && threadIdx.x < G) {
-    const int r = threadIdx.x;
-    float M = -INFINITY;
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][r]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float Ls = 0.f;
-    for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
-    a.partial_lse[(head0 + r) * a.max_partitions + p] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
-  }
+  __shared__ float lds[DecodeMergeLds<D, NT>::kFloats];
+  decode_partition<Tile, D, NT, OutT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // ---------------------------------------------------------------------------

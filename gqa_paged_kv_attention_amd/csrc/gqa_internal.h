@@ -115,9 +115,34 @@ hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32,
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,
                           hipStream_t stream);
-// bf16 prefill with K/V tiles shared through LDS.
+// Mixed batch, bf16: the scheduling pass writes the work units, ordered by
+// decreasing cost; the fused kernel runs unit i / Hkv for kv head i % Hkv.
+// Rows of a prefill unit (depends only on the build):
 int prefill_lds_rows_per_group();
-hipError_t launch_prefill_lds(const PrefillArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream);
+struct ScheduleArgs {
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  int2* units;                      // [unit_capacity] {sequence, code}: code >= 0 prefill row tile,
+                                    // code < 0 decode partition -1 - code
+  int* unit_count;
+  int unit_capacity;
+  int num_seqs;
+  int num_tokens;
+  int max_query_len;
+  int group;
+  int rows_per_group;
+  int max_blocks_per_seq;
+  int partition_size;               // decode partitions (tokens, multiple of 32)
+  int max_partitions;
+};
+struct MixedArgs {
+  PrefillArgs prefill;
+  DecodeArgs decode;
+  const int2* units;
+  const int* unit_count;
+};
+hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream);
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream);
 

@@ -1,11 +1,16 @@
-// Chunked prefill over the paged cache, bf16, with K/V tiles shared in LDS.
+// Mixed chunked-prefill + decode batch over the paged cache, bf16: a
+// scheduling pass and one fused kernel.
 //
 // The mixed batch of "[Kernel] [V1] Further optimizations to ROCm (Triton)
 // Backend to better handle GQA" (vLLM PR #14431, review thread on
-// chunked_prefill_paged_decode) runs a prefill kernel over the sequences with
-// more than one new token; each new token attends causally to the cached prefix
-// and to the chunk's earlier tokens (bottom-right aligned).
+// chunked_prefill_paged_decode) holds sequences with more than one new token
+// (prefill chunks: each new token attends causally to the cached prefix and to
+// the chunk's earlier tokens, bottom-right aligned) and sequences with one new
+// token (decodes), which the thread runs as a prefill kernel plus a decode
+// kernel launched alongside it.  Here both kinds of work are units of one
+// launch, ordered by a scheduling pass (below).
 //
+// Prefill units:
 // GQA packing: the rows of a (sequence, kv head) are the pairs (new token j,
 // query head g of the group), r = j * G + g, so the G heads that share a kv
 // head share every K/V tile that is loaded ("[Performance] Use optimized
@@ -21,15 +26,12 @@
 //   saturate at 65504, a precondition of this path).
 // The softmax denominator is the same product with V replaced by ones, so it
 // sums exactly the rounded P that weighs V and costs no VALU additions.
-#include "gqa_common.h"
-#include "gqa_internal.h"
+#include "decode_core.h"
 
 namespace gqa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr float kLazyRescale = 8.f;      // log2 growth of a row max before O is rescaled
 
 template <int D, int NTW>
@@ -121,23 +123,14 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
   }
 }
 
+// Row tile rt (rows [rt * R, rt * R + R) of the r = j * G + g order, R =
+// kRowsPerGroup) of sequence b against kv head kv.  sK / sV: two LDS buffers
+// each of kTile * KROW and D * VROW elements.
 template <int D, int NTW, class OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NTW <= 2 ? 2 : 1)))
-void prefill_lds_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int kv, uint16_t* sK, uint16_t* sV) {
   typedef PrefillLds<D, NTW> S;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * S::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * S::VROW];
-  __shared__ int s_scan[kThreads];
-  __shared__ int s_found[2];
-
+  constexpr int KBUF = kTile * S::KROW, VBUF = D * S::VROW;
   const int G = a.group;
-  const int kv = blockIdx.x % a.num_kv_heads;
-  const int tile = blockIdx.x / a.num_kv_heads;
-  int local = 0;
-  const int b = uniform(
-      locate_prefill_tile(a.query_start_loc, a.num_seqs, G, S::kRowsPerGroup, tile, s_scan, s_found, &local));
-  local = uniform(local);
-  if (b < 0) return;
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0) return;
@@ -145,8 +138,6 @@ void prefill_lds_kernel(PrefillArgs a) {
   const int prior = L - q_len;
   if (prior < 0) return;
   const int rows_total = q_len * G;
-  const int n_row_tiles = (rows_total + S::kRowsPerGroup - 1) / S::kRowsPerGroup;
-  const int rt = n_row_tiles - 1 - local;        // heaviest row tile of the sequence first
 
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, q = lane >> 4;
@@ -224,7 +215,7 @@ void prefill_lds_kernel(PrefillArgs a) {
   int rawA, rawB;
   fetch_pages(0, rawA, rawB);
   issue(page_id(rawA), page_id(rawB), kreg, vreg);
-  store_tile_lds<D, NTW>(sK[0], sV[0], kreg, vreg, plan, 0, L, kTile > L);
+  store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kTile > L);
   fetch_pages(1, rawA, rawB);
   __syncthreads();
 
@@ -301,8 +292,10 @@ void prefill_lds_kernel(PrefillArgs a) {
     const int pA = page_id(rawA), pB = page_id(rawB);
     if (more) issue(pA, pB, kreg, vreg);
     fetch_pages(it + 2, rawA, rawB);
-    if (tb <= lim_hi) compute(sK[buf], sV[buf], tb, tb + kTile - 1 > lim_lo);
-    if (more) store_tile_lds<D, NTW>(sK[buf ^ 1], sV[buf ^ 1], kreg, vreg, plan, tb + kTile, L, tb + 2 * kTile > L);
+    if (tb <= lim_hi) compute(sK + buf * KBUF, sV + buf * VBUF, tb, tb + kTile - 1 > lim_lo);
+    if (more)
+      store_tile_lds<D, NTW>(sK + (buf ^ 1) * KBUF, sV + (buf ^ 1) * VBUF, kreg, vreg, plan, tb + kTile, L,
+                             tb + 2 * kTile > L);
     __syncthreads();
   }
 
@@ -323,12 +316,132 @@ void prefill_lds_kernel(PrefillArgs a) {
 
 constexpr int kLdsNTW = 2;
 
-template <class OutT>
-hipError_t dispatch(const PrefillArgs& a, int D, int groups, hipStream_t s) {
-  if (D == 64)
-    hipLaunchKernelGGL((prefill_lds_kernel<64, kLdsNTW, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+// ---------------------------------------------------------------------------
+// Scheduling pass.  The mixed batch splits into work units, each run by one
+// work-group per kv head: a prefill row tile of a sequence with q_len > 1, or
+// a decode partition of a sequence with q_len = 1.  Their costs differ by
+// orders of magnitude (a row tile near the end of a long chunk reads the whole
+// prefix; most decodes read a few pages), and work-groups are dispatched in
+// index order, so the list is ordered by decreasing cost (longest processing
+// time first): the long units start first and the short ones fill in behind
+// them.  Cost, in tile steps of a work-group: a prefill row tile takes one step
+// per 32-key tile up to its last row's causal limit; a decode partition's
+// tiles are shared by the 4 waves.  One work-group of 1024 threads counts the
+// units per cost bucket in LDS, scans, and scatters (order within a bucket is
+// arbitrary; each unit's result does not depend on it).
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+constexpr int kCostBuckets = 4096;
+
+__device__ __forceinline__ int unit_cost_bucket(int c) { return min(c, kCostBuckets - 1); }
+
+template <class F>
+__device__ __forceinline__ void for_each_unit(const ScheduleArgs& a, int b, F&& emit) {
+  const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+  const int q_len = q1 - q0;
+  if (q1 > a.num_tokens || q0 < 0 || q_len <= 0 || q_len > a.max_query_len) return;
+  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
+  if (q_len == 1) {
+    const int Lp = min(L, a.max_partitions * a.partition_size);
+    const int nparts = max(1, (Lp + a.partition_size - 1) / a.partition_size);
+    const int tiles_all = (Lp + kTile - 1) / kTile;
+    const int per = tiles_all / nparts, extra = tiles_all % nparts;
+    for (int p = 0; p < nparts; ++p) {
+      const int t = per + (p < extra ? 1 : 0);
+      emit(b, -1 - p, (t + 3) / 4);
+    }
+    return;
+  }
+  const int prior = L - q_len;
+  if (prior < 0) return;
+  const int G = a.group, R = a.rows_per_group;
+  const int n_rt = (q_len * G + R - 1) / R;
+  for (int rt = n_rt - 1; rt >= 0; --rt) {
+    const int hi = prior + min(q_len - 1, (rt * R + R - 1) / G);
+    emit(b, rt, hi / kTile + 1);
+  }
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
+  __shared__ int hist[kCostBuckets];
+  __shared__ int part[kSchedThreads];
+  for (int i = threadIdx.x; i < kCostBuckets; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads)
+    for_each_unit(a, b, [&](int, int, int c) { atomicAdd(&hist[unit_cost_bucket(c)], 1); });
+  __syncthreads();
+  // exclusive scan in decreasing cost: start[c] = number of units costlier than c
+  constexpr int PER = kCostBuckets / kSchedThreads;
+  const int top = kCostBuckets - 1 - PER * threadIdx.x;       // this thread's buckets: top, top-1, ...
+  int local[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    local[i] = hist[top - i];
+    sum += local[i];
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int total = part[kSchedThreads - 1];
+  int run = part[threadIdx.x] - sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hist[top - i] = run;
+    run += local[i];
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads)
+    for_each_unit(a, b, [&](int bb, int code, int c) {
+      const int pos = atomicAdd(&hist[unit_cost_bucket(c)], 1);
+      if (pos < a.unit_capacity) a.units[pos] = make_int2(bb, code);
+    });
+  if (threadIdx.x == 0) *a.unit_count = min(total, a.unit_capacity);
+}
+
+// ---------------------------------------------------------------------------
+// Mixed batch: work-group i runs unit i / Hkv of the scheduled list for kv
+// head i % Hkv, as a prefill row tile (K/V tiles shared through LDS) or as a
+// decode partition (per-wave tile pipeline, waves merged through LDS).  The
+// decode units ride along the prefill ones in one launch: HBM-bound decodes
+// and matrix-bound prefill tiles then share the device instead of running one
+// after the other.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+struct MixedLds {
+  typedef PrefillLds<D, kLdsNTW> S;
+  static constexpr int kPrefillBytes = 2 * (kTile * S::KROW + D * S::VROW) * 2;
+  static constexpr int kDecodeBytes = DecodeMergeLds<D, NT>::kFloats * 4;
+  static constexpr int kBytes = kPrefillBytes > kDecodeBytes ? kPrefillBytes : kDecodeBytes;
+};
+
+template <int D, int NT, class OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+void mixed_kernel(MixedArgs a) {
+  typedef PrefillLds<D, kLdsNTW> S;
+  __shared__ __attribute__((aligned(16))) char lds[MixedLds<D, NT>::kBytes];
+  const int Hkv = a.prefill.num_kv_heads;
+  const int slot = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
+  if (slot >= *a.unit_count) return;
+  const int2 u = a.units[slot];
+  if (u.y >= 0) {
+    uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
+    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, kv, sK, sK + 2 * kTile * S::KROW);
+  } else {
+    decode_partition<TileBF16<D>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, reinterpret_cast<float*>(lds));
+  }
+}
+
+template <int D, class OutT>
+hipError_t mixed_dispatch(const MixedArgs& a, int groups, hipStream_t s) {
+  if (a.prefill.group <= 16)
+    hipLaunchKernelGGL((mixed_kernel<D, 1, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_lds_kernel<128, kLdsNTW, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mixed_kernel<D, 2, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -336,9 +449,15 @@ hipError_t dispatch(const PrefillArgs& a, int D, int groups, hipStream_t s) {
 
 int prefill_lds_rows_per_group() { return PrefillLds<128, kLdsNTW>::kRowsPerGroup; }
 
-hipError_t launch_prefill_lds(const PrefillArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream) {
-  return out_f32 ? dispatch<float>(a, head_dim, grid_groups, stream)
-                 : dispatch<uint16_t>(a, head_dim, grid_groups, stream);
+hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream) {
+  if (head_dim == 64)
+    return out_f32 ? mixed_dispatch<64, float>(a, grid_groups, stream) : mixed_dispatch<64, uint16_t>(a, grid_groups, stream);
+  return out_f32 ? mixed_dispatch<128, float>(a, grid_groups, stream) : mixed_dispatch<128, uint16_t>(a, grid_groups, stream);
 }
 
 }  // namespace gqa

@@ -60,7 +60,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_decode.restype = i32
     lib.splitk_lse_reduce.argtypes = [vp, vp, vp, vp, vp, Dims, i32, i32, i32, vp]
     lib.splitk_lse_reduce.restype = i32
-    lib.chunked_prefill_paged_decode_workspace_size.argtypes = [Dims, i32, i32]
+    lib.chunked_prefill_paged_decode_workspace_size.argtypes = [Dims, i32, i32, i32]
     lib.chunked_prefill_paged_decode_workspace_size.restype = sz
     lib.chunked_prefill_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, Dims, f32, i32, vp, sz,
                                                  vp]
@@ -152,12 +152,16 @@ def decode_workspace_size(dims: Dims, max_seq_len: int, partition_size: int) -> 
     return int(load_library().paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
 
 
+def mixed_workspace_size(dims: Dims, num_tokens: int, max_seq_len: int, partition_size: int) -> int:
+    return int(load_library().chunked_prefill_paged_decode_workspace_size(dims, int(num_tokens), int(max_seq_len),
+                                                                          int(partition_size)))
+
+
 def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        # the leading counter area must start at zero; every call leaves it zero
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     # a smaller workspace is passed through: the library either adapts (balanced
     # split: fewer waves) or returns GQA_ERR_WORKSPACE
     return workspace, workspace.numel() * workspace.element_size()
@@ -219,7 +223,7 @@ def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, se
         out = torch.empty(T, Hq, d, dtype=out_dtype, device=query.device)
     dims = make_dims(num_seqs=seq_lens.shape[0], num_heads=Hq, key_cache=key_cache, block_tables=block_tables,
                      q_dtype=query.dtype, out_dtype=out_dtype)
-    nbytes = int(lib.chunked_prefill_paged_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
+    nbytes = int(lib.chunked_prefill_paged_decode_workspace_size(dims, T, int(max_seq_len), int(partition_size)))
     ws, wsb = _workspace(nbytes, query.device, workspace)
     _call("chunked_prefill_paged_decode",
           lib.chunked_prefill_paged_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),

@@ -176,12 +176,28 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
  * prefix) and decodes (q_len == 1), all over the same paged cache ("[Kernel]
  * [V1] Further optimizations to ROCm (Triton) Backend to better handle GQA",
  * review thread: the prefill kernel skips single-token sequences, which a
- * decode kernel handles).  query/out are [num_tokens, num_heads, head_dim];
- * max_query_len and max_seq_len are host-side bounds.  Sequences with q_len 0
- * produce no rows.  Decodes are split into partitions of partition_size tokens
- * as in paged_gqa_decode (0 = no split).
+ * decode kernel handles alongside it).  query/out are [num_tokens, num_heads,
+ * head_dim]; max_query_len and max_seq_len are host-side bounds (sequences
+ * whose q_len exceeds max_query_len are not computed).  Sequences with
+ * q_len 0 produce no rows.
+ *
+ * bf16: a one-work-group scheduling pass lists the work units (prefill row
+ * tiles of 128 (token, head) rows and decode partitions) in decreasing order
+ * of cost, and one fused kernel runs them, so decodes proceed alongside the
+ * prefill tiles; a merge kernel follows when decodes are split.  Decodes are
+ * split into partitions of partition_size tokens (merged by log-sum-exp in
+ * partition order); partition_size == 0 lets the library pick (partitions of
+ * 4096 tokens, i.e. no split unless max_seq_len > 4096).  Prefill rows compute
+ * P.V on fp16 matrix cores (P rounded to fp16, V converted from bf16):
+ * precondition |V| < 65504, else results saturate.
+ * fp32: a prefill kernel, then the decode of paged_gqa_decode (same meaning of
+ * partition_size).
+ *
+ * Workspace (device, >= chunked_prefill_paged_decode_workspace_size bytes for
+ * the same dims, num_tokens, max_seq_len and partition_size; 256-byte
+ * aligned; no initialisation needed): the unit list and split partials.
  */
-size_t chunked_prefill_paged_decode_workspace_size(gqa_dims dims, int32_t max_seq_len,
+size_t chunked_prefill_paged_decode_workspace_size(gqa_dims dims, int32_t num_tokens, int32_t max_seq_len,
                                                    int32_t partition_size);
 int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* key_cache,
                                      const void* value_cache, const int32_t* block_tables,

@@ -77,7 +77,9 @@ def test_workspace_size_and_check(lib):
     assert n >= rows * 128 * 4 + rows * 4 and n % 256 == 0
     assert decode(lib, d, max_seq_len=4096, partition=512) == WORKSPACE
     assert decode(lib, d, max_seq_len=4096, partition=512, ws=FAKE, wsb=n - 1) == WORKSPACE
-    assert lib.chunked_prefill_paged_decode_workspace_size(d, 4096, 512) == n
+    f32 = dims(q_dtype=ops.GQA_F32, kv_dtype=ops.GQA_F32)
+    assert lib.chunked_prefill_paged_decode_workspace_size(f32, 100, 4096, 512) == \
+        lib.paged_gqa_decode_workspace_size(f32, 4096, 512)
     # balanced split: prefix table plus two segment slots per worker (at least one work-group's worth)
     s = lib.paged_gqa_decode_workspace_size(d, 4096, 0)
     assert s >= 4 * 2 * 4 * (128 + 1) * 4 and s % 256 == 0
@@ -101,3 +103,21 @@ def test_mixed_and_reduce_validation(lib):
     assert lib.reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, d, None) == INVALID
     assert lib.splitk_lse_reduce(FAKE, FAKE, FAKE, FAKE, None, d, 0, 512, 1, None) == INVALID
     assert lib.splitk_lse_reduce(FAKE, FAKE, FAKE, FAKE, None, d, 4, 0, 1, None) == INVALID
+
+
+def test_mixed_bf16_workspace(lib):
+    """bf16 mixed batches need the scheduled unit list (8 bytes per unit, at
+    least num_tokens * G / 128 prefill row tiles plus one unit per decode), a
+    count, and partials only when decodes are split."""
+    d = dims()                                     # 4 seqs, G = 4, bf16
+    n = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 256, 0)
+    assert n % 256 == 0 and n >= (1000 * 4 // 128 + 4) * 8 + 4
+    # bigger batches need more list; a split adds the partials
+    assert lib.chunked_prefill_paged_decode_workspace_size(d, 4000, 256, 0) > n
+    split = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 8192, 512)
+    assert split >= n + 4 * 32 * 16 * 128 * 4
+    call = lambda ws, wsb: lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 100, 256,
+                                                            d, 0.1, 0, ws, wsb, None)
+    assert call(None, 0) == WORKSPACE
+    assert call(FAKE, n - 1) == WORKSPACE
+    assert lib.chunked_prefill_paged_decode_workspace_size(d, -1, 256, 0) == 0
