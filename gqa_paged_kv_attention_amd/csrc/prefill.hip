@@ -33,6 +33,8 @@ namespace gqa {
 namespace {
 
 constexpr float kLazyRescale = 8.f;      // log2 growth of a row max before O is rescaled
+constexpr int kKeyTile = 64;             // keys per iteration: four pages
+constexpr int kTilePages = kKeyTile / kPage;
 
 template <int D, int NTW>
 struct PrefillLds {
@@ -40,64 +42,75 @@ struct PrefillLds {
   static constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
   static constexpr int KC = D / 32;                 // 16-byte chunks of a row per Q.K^T product
   static constexpr int DT = D / 16;                 // 16-channel output blocks
-  static constexpr int KROW = D + 8;                // LDS row stride of the key tile (elements)
-  static constexpr int VROW = kTile + 8;            // LDS row stride of the value tile (elements)
-  static constexpr int KCH = kTile * D / 8 / kThreads;   // 16-byte key chunks per thread per tile
-  static constexpr int VCH = 2 * D * 2 / kThreads;       // 16-byte value chunks per thread per tile
+  static constexpr int KROW = D + 16;               // LDS row stride of the key tile (elements)
+  static constexpr int VROW = kKeyTile + 16;        // LDS row stride of the value tile (elements)
+  static constexpr int KBUF = kKeyTile * KROW;      // one key buffer (elements)
+  static constexpr int VBUF = D * VROW;             // one value buffer (elements)
+  static constexpr int kBytes = 2 * (KBUF + VBUF) * 2;
+  static constexpr int CH = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile, K and V each
+  // chunk i of a thread comes from page i * PI + (thread / (kThreads / PI)) of the tile
+  static constexpr int PI = 128 / D;
 };
 
-// LDS row of key token t.  A 128-bit LDS read is served 8 lanes at a time over
-// 32 four-byte banks, so with a 272-byte row stride row r lands in 16-byte bank
-// group r mod 8.  Lanes 0-7 of a Q.K^T product read tokens {0-3, 8-11} (+4, +16
-// for lanes 8-15): flipping bit 2 of tokens whose bit 3 is set sends those runs
-// to distinct groups.
-__device__ __forceinline__ int key_row(int t) { return t ^ ((t >> 1) & 4); }
+// LDS banking (gfx950, measured): a 128-bit access is served 32 lanes at a
+// time by 128 four-byte banks, so the 32 lanes' 16-byte slots must differ mod
+// 512 bytes.  Key rows are D + 16 elements apart (an even number of slots whose
+// half is odd: 18 for D = 128, 10 for D = 64), so rows that differ mod 16 land
+// on distinct even slots and the two 16-byte chunks of a 32-lane group fill the
+// odd ones.  Lanes 0-15 of a Q.K^T product read tokens {0-3, 8-11, 16-19,
+// 24-27} (+4 for the second product, +32 for the second half of the tile):
+// moving bit 4 of the token onto bit 2 makes them distinct mod 16.  Value rows
+// (channels) are kKeyTile + 16 elements apart (10 slots): 16 consecutive
+// channels land on distinct even slots as well.
+__device__ __forceinline__ int key_row(int t) { return t ^ ((t >> 2) & 4); }
 
-// max without the NaN canonicalisation fmaxf implies (operands are never NaN
-// here: masked scores are -inf, not NaN)
-__device__ __forceinline__ float max2(float a, float b) { return a > b ? a : b; }
-
-// This thread's share of a tile: for each 16-byte chunk, the page it comes from
-// (0 = first page of the tile, 1 = second), its element offset inside that
-// page, and its element offset in the LDS tile.
+// This thread's share of a tile: for each 16-byte chunk of keys and of values,
+// its element offset inside its page and in the LDS tile.  The chunk's page is
+// wave-uniform: i * PI + pw.
 template <int D, int NTW>
 struct TileCopyPlan {
   typedef PrefillLds<D, NTW> S;
-  // k_page / v_page are wave-uniform: 16 tokens of keys (or 16 tokens of one
-  // page's values) are a multiple of a wave's 64 chunks for D = 64 and 128
-  int k_page[S::KCH], k_src[S::KCH], k_dst[S::KCH];
-  int v_page[S::VCH], v_src[S::VCH], v_dst[S::VCH], v_tok[S::VCH];
+  int k_src[S::CH], k_dst[S::CH];
+  int v_src[S::CH], v_dst[S::CH], v_tok[S::CH];
+  int pw;                                           // wave-uniform page offset of chunk 0
   __device__ __forceinline__ void init() {
+    pw = S::PI == 1 ? 0 : uniform(threadIdx.x / (kThreads / S::PI));
 #pragma unroll
-    for (int i = 0; i < S::KCH; ++i) {
+    for (int i = 0; i < S::CH; ++i) {
       const int ci = threadIdx.x + i * kThreads;
-      const int token = ci / (D / 8), col = ci % (D / 8);
-      k_page[i] = uniform(token / kPage);
+      const int token = ci / (D / 8), col = ci % (D / 8);        // token / 16: page of chunk i
       k_src[i] = (token % kPage) * D + col * 8;
       k_dst[i] = key_row(token) * S::KROW + col * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < S::VCH; ++i) {
-      const int ci = threadIdx.x + i * kThreads;
-      const int h = ci / (2 * D), rem = ci % (2 * D);
+      const int h = ci / (2 * D), rem = ci % (2 * D);            // h: page of chunk i
       const int d = rem / 2, e = rem % 2;
-      v_page[i] = uniform(h);
       v_src[i] = d * kPage + 8 * e;
       v_dst[i] = d * S::VROW + 16 * h + 8 * e;
       v_tok[i] = 16 * h + 8 * e;                     // first token (in the tile) of this 8-token run
     }
   }
+  // base pointer of chunk i (constant indices only, so TilePtrs stays in registers)
+  template <class P>
+  __device__ __forceinline__ P page_of(int i, const P* pages) const {
+    if (S::PI == 1) return pages[i];
+    return pw ? pages[i * S::PI + 1] : pages[i * S::PI];
+  }
+};
+
+// Page base pointers (K and V, this kv head) of the four pages of a tile.
+struct TilePtrs {
+  const uint16_t* k[kTilePages];
+  const uint16_t* v[kTilePages];
 };
 
 template <int D, int NTW>
 __device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW>& plan,
-                                               const uint16_t* kA, const uint16_t* kB, const uint16_t* vA,
-                                               const uint16_t* vB) {
+                                               const TilePtrs& tp) {
   typedef PrefillLds<D, NTW> S;
 #pragma unroll
-  for (int i = 0; i < S::KCH; ++i) kreg[i] = ld16((plan.k_page[i] ? kB : kA) + plan.k_src[i]);
-#pragma unroll
-  for (int i = 0; i < S::VCH; ++i) vreg[i] = ld16((plan.v_page[i] ? vB : vA) + plan.v_src[i]);
+  for (int i = 0; i < S::CH; ++i) {
+    kreg[i] = ld16(plan.page_of(i, tp.k) + plan.k_src[i]);
+    vreg[i] = ld16(plan.page_of(i, tp.v) + plan.v_src[i]);
+  }
 }
 
 // Registers -> LDS; values are converted to fp16, and with `tail` set those of
@@ -107,9 +120,9 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
                                                const TileCopyPlan<D, NTW>& plan, int tile_base, int L, bool tail) {
   typedef PrefillLds<D, NTW> S;
 #pragma unroll
-  for (int i = 0; i < S::KCH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
+  for (int i = 0; i < S::CH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
 #pragma unroll
-  for (int i = 0; i < S::VCH; ++i) {
+  for (int i = 0; i < S::CH; ++i) {
     uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
     if (tail) {
       const int t0 = tile_base + plan.v_tok[i];
@@ -125,11 +138,10 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 
 // Row tile rt (rows [rt * R, rt * R + R) of the r = j * G + g order, R =
 // kRowsPerGroup) of sequence b against kv head kv.  sK / sV: two LDS buffers
-// each of kTile * KROW and D * VROW elements.
+// of KBUF and VBUF elements each.
 template <int D, int NTW, class OutT>
 __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int kv, uint16_t* sK, uint16_t* sV) {
   typedef PrefillLds<D, NTW> S;
-  constexpr int KBUF = kTile * S::KROW, VBUF = D * S::VROW;
   const int G = a.group;
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
@@ -177,27 +189,33 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   const int lim_lo = prior + r0 / G;
   const int lim_hi = wave_rows ? prior + min(q_len - 1, (r0 + S::kRowsPerWave - 1) / G) : -1;
   const int group_hi = prior + min(q_len - 1, (rt * S::kRowsPerGroup + S::kRowsPerGroup - 1) / G);
-  const int n_tiles = group_hi / kTile + 1;
+  const int n_tiles = group_hi / kKeyTile + 1;
   const int npages = (L + kPage - 1) / kPage;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache) + (size_t)kv * (kPage * D);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache) + (size_t)kv * (kPage * D);
-  const size_t page_stride = (size_t)a.num_kv_heads * (kPage * D);
+  const char* kc = reinterpret_cast<const char*>(a.key_cache) + (size_t)kv * (kPage * D * 2);
+  const char* vc = reinterpret_cast<const char*>(a.value_cache) + (size_t)kv * (kPage * D * 2);
+  const uint32_t page_bytes = (uint32_t)a.num_kv_heads * (kPage * D * 2);
 
   TileCopyPlan<D, NTW> plan;
   plan.init();
-  // Raw block-table entries of tile t (clamped to the last tile).  They are
-  // loaded one iteration before they are used, so that waiting for them never
-  // waits for the K/V loads issued just before.
-  auto fetch_pages = [&](int t, int& rawA, int& rawB) {
-    const int pg = min(t, n_tiles - 1) * 2;
-    rawA = bt[pg];
-    rawB = bt[min(pg + 1, npages - 1)];
+  // Raw block-table entries of tile t (clamped to the last tile and page).
+  // They are loaded one iteration before they are used, so that waiting for
+  // them never waits for the K/V loads issued just before.
+  auto fetch_pages = [&](int t, int* raw) {
+    const int pg = min(t, n_tiles - 1) * kTilePages;
+#pragma unroll
+    for (int j = 0; j < kTilePages; ++j) raw[j] = bt[min(pg + j, npages - 1)];
   };
-  auto page_id = [&](int raw) { return uniform((unsigned)raw < (unsigned)a.num_blocks ? raw : 0); };
-  auto issue = [&](int pA, int pB, uint4* kr, uint4* vr) {
-    load_tile_regs<D, NTW>(kr, vr, plan, kc + pA * page_stride, kc + pB * page_stride, vc + pA * page_stride,
-                           vc + pB * page_stride);
+  auto issue = [&](const int* raw, uint4* kr, uint4* vr) {
+    TilePtrs tp;
+#pragma unroll
+    for (int j = 0; j < kTilePages; ++j) {
+      const uint32_t pid = (uint32_t)uniform((unsigned)raw[j] < (unsigned)a.num_blocks ? raw[j] : 0);
+      const size_t off = (size_t)pid * page_bytes;
+      tp.k[j] = reinterpret_cast<const uint16_t*>(kc + off);
+      tp.v[j] = reinterpret_cast<const uint16_t*>(vc + off);
+    }
+    load_tile_regs<D, NTW>(kr, vr, plan, tp);
   };
 
   float m[NTW], mu[NTW];
@@ -211,91 +229,123 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
     for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] = zero4();
   }
 
-  uint4 kreg[S::KCH], vreg[S::VCH];
-  int rawA, rawB;
-  fetch_pages(0, rawA, rawB);
-  issue(page_id(rawA), page_id(rawB), kreg, vreg);
-  store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kTile > L);
-  fetch_pages(1, rawA, rawB);
+  // Pipeline: tile t is loaded into registers during iteration t - 2, written
+  // to LDS buffer t & 1 at the top of iteration t - 1 and consumed in
+  // iteration t, so each load has a whole iteration to arrive.
+  uint4 kreg[S::CH], vreg[S::CH];
+  int raw[kTilePages];
+  fetch_pages(0, raw);
+  issue(raw, kreg, vreg);
+  fetch_pages(1, raw);
+  store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kKeyTile > L);
+  if (n_tiles > 1) issue(raw, kreg, vreg);
+  fetch_pages(2, raw);
   __syncthreads();
 
-  // LDS offsets of this lane's key rows (products s = 0, 1; token fed to row m
-  // as in TileBF16) and value rows
+  // LDS offsets of this lane's key rows (32-key half 0, products s = 0, 1;
+  // token fed to row m as in TileBF16; half 1 is 32 rows further) and value
+  // rows
   const int kslot = ((n < 8) ? 0 : kPage) + (n & 3) + 8 * ((n >> 2) & 1);
   const int koff0 = key_row(kslot) * S::KROW + 8 * q, koff1 = key_row(kslot + 4) * S::KROW + 8 * q;
   const int voff = n * S::VROW + 8 * q;
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0 x 8
   const float pinf = opaque(INFINITY);
 
-  // One tile against this wave's rows; `masked` applies the causal limit per
-  // score (tiles wholly below the diagonal skip it).
+  // One 64-key tile against this wave's rows; `masked` applies the causal
+  // limit per score (tiles wholly below the diagonal skip it).  Scores of
+  // half hf, product s sit at keys 32 hf + 8 q + 4 s + i (i = 0..3).
   auto compute = [&](const uint16_t* K, const uint16_t* V, int tb, bool masked) {
-    f32x4_t acc[NTW][2];
+    f32x4_t acc[NTW][4];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero4();
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[nt][x] = zero4();
 #pragma unroll
     for (int c = 0; c < S::KC; ++c) {
-      const uint4 k0 = *reinterpret_cast<const uint4*>(K + koff0 + 32 * c);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(K + koff1 + 32 * c);
+      uint4 kf[4];
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        acc[nt][0] = mfma_bf16(k0, qf[nt][c], acc[nt][0]);
-        acc[nt][1] = mfma_bf16(k1, qf[nt][c], acc[nt][1]);
-      }
+      for (int x = 0; x < 4; ++x)
+        kf[x] = *reinterpret_cast<const uint4*>(K + (x >> 1) * 32 * S::KROW + ((x & 1) ? koff1 : koff0) + 32 * c);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[nt][x] = mfma_bf16(kf[x], qf[nt][c], acc[nt][x]);
     }
-    uint4 pf[NTW];
+    float sc[NTW][16], mx[NTW];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      float sc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = i < 4 ? acc[nt][0][i] : acc[nt][1][i - 4];
+      for (int i = 0; i < 16; ++i) sc[nt][i] = acc[nt][i >> 2][i & 3];
       if (masked) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sc[i] = (tb + 8 * q + i <= lim[nt]) ? sc[i] : -INFINITY;
+        for (int i = 0; i < 16; ++i)
+          sc[nt][i] = (tb + 32 * (i >> 3) + 8 * q + (i & 7) <= lim[nt]) ? sc[nt][i] : -INFINITY;
       }
-      const float mx = fmax_nn(fmax_nn(fmax_nn(sc[0], sc[1], pinf), fmax_nn(sc[2], sc[3], pinf), pinf),
-                               fmax_nn(fmax_nn(sc[4], sc[5], pinf), fmax_nn(sc[6], sc[7], pinf), pinf), pinf);
-      // Running max in log2 units, raised (and O rescaled) only when some row's
-      // max grows by more than kLazyRescale, so P stays <= 2^kLazyRescale.  A
-      // lane's own max decides whether any row needs it; only then is the row
-      // max taken across the row's four lanes.
-      if (__any(mx * sl2 > m[nt] + kLazyRescale)) {
-        const float m_new = fmax_nn(m[nt], row_max4(mx) * sl2, pinf);
-        const float mu_new = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m[nt] - mu_new);     // 0 while m = -inf (O and l are 0)
-        ol[nt] *= alpha;
+      float t8[8];
 #pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] *= alpha;
-        m[nt] = m_new;
-        mu[nt] = mu_new;
+      for (int i = 0; i < 8; ++i) t8[i] = fmax_nn(sc[nt][2 * i], sc[nt][2 * i + 1], pinf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t8[i] = fmax_nn(t8[2 * i], t8[2 * i + 1], pinf);
+      mx[nt] = fmax_nn(fmax_nn(t8[0], t8[1], pinf), fmax_nn(t8[2], t8[3], pinf), pinf);
+      grow |= mx[nt] * sl2 > m[nt] + kLazyRescale;
+    }
+    // Running max in log2 units, raised (and O rescaled) only when some row's
+    // max grows by more than kLazyRescale, so P stays <= 2^kLazyRescale.  A
+    // lane's own max decides whether any row needs it; only then is the row
+    // max taken across the row's four lanes.
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const float m_new = fmax_nn(m[nt], row_max4(mx[nt]) * sl2, pinf);
+        if (m_new > m[nt] + kLazyRescale) {
+          const float mu_new = m_new;
+          const float alpha = fast_exp2(m[nt] - mu_new);   // 0 while m = -inf (O and l are 0)
+          ol[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < S::DT; ++dt) o[nt][dt] *= alpha;
+          m[nt] = m_new;
+          mu[nt] = mu_new;
+        }
       }
+    }
+    uint4 pf[NTW][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = fast_exp2(__builtin_fmaf(sc[i], sl2, -mu[nt]));
-      pf[nt] = make_uint4(f32x2_to_f16x2(sc[0], sc[1]), f32x2_to_f16x2(sc[2], sc[3]), f32x2_to_f16x2(sc[4], sc[5]),
-                          f32x2_to_f16x2(sc[6], sc[7]));
-      ol[nt] = mfma_f16(ones, pf[nt], ol[nt]);
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[nt][i] = fast_exp2(__builtin_fmaf(sc[nt][i], sl2, -mu[nt]));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float* x = sc[nt] + 8 * hf;
+        pf[nt][hf] = make_uint4(f32x2_to_f16x2(x[0], x[1]), f32x2_to_f16x2(x[2], x[3]), f32x2_to_f16x2(x[4], x[5]),
+                                f32x2_to_f16x2(x[6], x[7]));
+        ol[nt] = mfma_f16(ones, pf[nt][hf], ol[nt]);
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
-      const uint4 vf = *reinterpret_cast<const uint4*>(V + voff + 16 * dt * S::VROW);
+      const uint4 v0 = *reinterpret_cast<const uint4*>(V + voff + 16 * dt * S::VROW);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(V + voff + 16 * dt * S::VROW + 32);
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) o[nt][dt] = mfma_f16(vf, pf[nt], o[nt][dt]);
+      for (int nt = 0; nt < NTW; ++nt) {
+        o[nt][dt] = mfma_f16(v0, pf[nt][0], o[nt][dt]);
+        o[nt][dt] = mfma_f16(v1, pf[nt][1], o[nt][dt]);
+      }
     }
   };
 
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
-    const int tb = it * kTile;
-    const bool more = it + 1 < n_tiles;
-    // tile it + 1: global loads in flight while tile it is computed; the
-    // block-table entries of tile it + 2 follow them
-    const int pA = page_id(rawA), pB = page_id(rawB);
-    if (more) issue(pA, pB, kreg, vreg);
-    fetch_pages(it + 2, rawA, rawB);
-    if (tb <= lim_hi) compute(sK + buf * KBUF, sV + buf * VBUF, tb, tb + kTile - 1 > lim_lo);
-    if (more)
-      store_tile_lds<D, NTW>(sK + (buf ^ 1) * KBUF, sV + (buf ^ 1) * VBUF, kreg, vreg, plan, tb + kTile, L,
-                             tb + 2 * kTile > L);
+    const int tb = it * kKeyTile;
+    // tile it + 1 (loaded during the previous iteration) -> the other buffer,
+    // which every wave finished reading before the last barrier; then the
+    // loads of tile it + 2, and the block-table entries of tile it + 3
+    if (it + 1 < n_tiles)
+      store_tile_lds<D, NTW>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan, tb + kKeyTile, L,
+                             tb + 2 * kKeyTile > L);
+    if (it + 2 < n_tiles) issue(raw, kreg, vreg);
+    fetch_pages(it + 3, raw);
+    if (tb <= lim_hi) compute(sK + buf * S::KBUF, sV + buf * S::VBUF, tb, tb + kKeyTile - 1 > lim_lo);
     __syncthreads();
   }
 
@@ -322,13 +372,19 @@ constexpr int kLdsNTW = 2;
 // a decode partition of a sequence with q_len = 1.  Their costs differ by
 // orders of magnitude (a row tile near the end of a long chunk reads the whole
 // prefix; most decodes read a few pages), and work-groups are dispatched in
-// index order, so the list is ordered by decreasing cost (longest processing
-// time first): the long units start first and the short ones fill in behind
-// them.  Cost, in tile steps of a work-group: a prefill row tile takes one step
-// per 32-key tile up to its last row's causal limit; a decode partition's
-// tiles are shared by the 4 waves.  One work-group of 1024 threads counts the
-// units per cost bucket in LDS, scans, and scatters (order within a bucket is
-// arbitrary; each unit's result does not depend on it).
+// index order, so sequences are listed by decreasing cost of their costliest
+// unit (longest processing time first): the long units start first and the
+// short ones fill in behind them.  A sequence's units stay contiguous, heaviest
+// first: its row tiles then run at the same time and stream the same K/V
+// pages, which they mostly find in L2 instead of each fetching the prefix from
+// HBM (work-group i goes to XCD i mod 8, so with Hkv a multiple of 8 all work-
+// groups of one kv head share an XCD and its L2).  Cost,
+// in tile steps of a work-group: a prefill row tile takes one step per 32-key
+// tile up to its last row's causal limit; a decode partition's tiles are
+// shared by the 4 waves.  One work-group of 1024 threads counts the units per
+// cost bucket in LDS, scans, and reserves a range per sequence (the order of
+// sequences within a bucket is arbitrary; each unit's result does not depend
+// on it).
 // ---------------------------------------------------------------------------
 constexpr int kSchedThreads = 1024;
 constexpr int kCostBuckets = 4096;
@@ -367,8 +423,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   __shared__ int part[kSchedThreads];
   for (int i = threadIdx.x; i < kCostBuckets; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
-  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads)
-    for_each_unit(a, b, [&](int, int, int c) { atomicAdd(&hist[unit_cost_bucket(c)], 1); });
+  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
+    int nu = 0, cmax = 0;
+    for_each_unit(a, b, [&](int, int, int c) { ++nu; cmax = max(cmax, c); });
+    if (nu) atomicAdd(&hist[unit_cost_bucket(cmax)], nu);
+  }
   __syncthreads();
   // exclusive scan in decreasing cost: start[c] = number of units costlier than c
   constexpr int PER = kCostBuckets / kSchedThreads;
@@ -395,11 +454,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     run += local[i];
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads)
-    for_each_unit(a, b, [&](int bb, int code, int c) {
-      const int pos = atomicAdd(&hist[unit_cost_bucket(c)], 1);
+  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
+    int nu = 0, cmax = 0;
+    for_each_unit(a, b, [&](int, int, int c) { ++nu; cmax = max(cmax, c); });
+    if (!nu) continue;
+    int pos = atomicAdd(&hist[unit_cost_bucket(cmax)], nu);    // a contiguous range for the sequence
+    for_each_unit(a, b, [&](int bb, int code, int) {
       if (pos < a.unit_capacity) a.units[pos] = make_int2(bb, code);
+      ++pos;
     });
+  }
   if (threadIdx.x == 0) *a.unit_count = min(total, a.unit_capacity);
 }
 
@@ -414,7 +478,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
 template <int D, int NT>
 struct MixedLds {
   typedef PrefillLds<D, kLdsNTW> S;
-  static constexpr int kPrefillBytes = 2 * (kTile * S::KROW + D * S::VROW) * 2;
+  static constexpr int kPrefillBytes = S::kBytes;
   static constexpr int kDecodeBytes = DecodeMergeLds<D, NT>::kFloats * 4;
   static constexpr int kBytes = kPrefillBytes > kDecodeBytes ? kPrefillBytes : kDecodeBytes;
 };
@@ -430,7 +494,7 @@ void mixed_kernel(MixedArgs a) {
   const int2 u = a.units[slot];
   if (u.y >= 0) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, kv, sK, sK + 2 * kTile * S::KROW);
+    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, kv, sK, sK + 2 * S::KBUF);
   } else {
     decode_partition<TileBF16<D>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, reinterpret_cast<float*>(lds));
   }
