@@ -12,10 +12,13 @@ stream), the mixed chunked-prefill + decode batch's tokens/s, and the CPU
 oracle's throughput on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
+       python bench.py --copy-calibration   (a plain 512 MiB device copy, for
+       scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,15 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
+
+# HBM traffic of one paged_gqa_decode call on this workload (both of its
+# kernels), from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch) over `bench.py --steps 20 --warmup 5 --no-mixed
+# --no-cpu-baseline`, each scaled by what the same counter reads for the
+# 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
+# sources it was measured on (their SHA-256 below); otherwise reported as null.
+DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
+DECODE_TRAFFIC = {"sources_sha256": "01d2971b0f194e4b3136d408692f31a5889a9a2310974395d679429e0f2e732b", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648983527, "write_bytes_per_call": 6338377, "hbm_bytes_per_call": 655321903, "fetch_factor": 1.99989, "write_factor": 1.0}
 
 
 def parse():
@@ -39,7 +51,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
+
+
+def decode_sources_sha256() -> str:
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gqa_paged_kv_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 512 MiB, repeated 5 times: it reads and
+    writes exactly 512 MiB per dispatch, the yardstick for the HBM counters."""
+    import torch
+    n = 512 << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}), flush=True)
 
 
 def event_time_ms(fn, reps, stream):
@@ -96,6 +131,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     ops.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -135,8 +173,12 @@ def main():
     # dominant kernel: the decode launch, timed with HIP events on its stream
     decode_ms = event_time_ms(decode, max(20, args.steps // 2), stream)
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    traffic = None
+    if DECODE_TRAFFIC is not None and DECODE_TRAFFIC["sources_sha256"] == decode_sources_sha256() \
+            and args.partition == DECODE_TRAFFIC["partition_size"] and args.seed == DECODE_TRAFFIC["seed"]:
+        traffic = DECODE_TRAFFIC["hbm_bytes_per_call"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "paged_gqa_decode call (balanced decode kernel + merge kernel)", "avg_ms": round(decode_ms, 5),
                 "bytes_per_launch": kv_bytes}
 
