@@ -104,7 +104,9 @@ bool mixed_decode_split(int32_t max_seq_len, int32_t partition_size, int* psize,
 }
 
 // Upper bound on scheduled units: prefill row tiles (at most one partial tile
-// per sequence beyond num_tokens * G / rows) plus decode partitions.
+// per sequence beyond num_tokens * G / rows) plus decode partitions.  The
+// scheduling pass places units exactly for lists below kMaxMixedUnits.
+constexpr long long kMaxMixedUnits = 1LL << 20;
 long long mixed_unit_capacity(const gqa_dims& d, int32_t num_tokens, int nparts) {
   const long long G = d.num_heads / d.num_kv_heads;
   const long long rows = gqa::prefill_lds_rows_per_group();
@@ -351,7 +353,7 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
     int psize = 0, nparts = 0;
     if (!mixed_decode_split(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
     const long long cap = mixed_unit_capacity(dims, num_tokens, nparts);
-    if (cap * dims.num_kv_heads > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    if (cap >= kMaxMixedUnits || cap * dims.num_kv_heads > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
     const size_t need = mixed_bytes(dims, num_tokens, max_seq_len, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
     char* ws = reinterpret_cast<char*>(workspace);

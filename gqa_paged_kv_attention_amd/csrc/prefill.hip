@@ -121,19 +121,28 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
   typedef PrefillLds<D, NTW> S;
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
+  uint32_t w[S::CH][4];
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) {
-    uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-    if (tail) {
+    w[i][0] = vreg[i].x;
+    w[i][1] = vreg[i].y;
+    w[i][2] = vreg[i].z;
+    w[i][3] = vreg[i].w;
+  }
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < S::CH; ++i) {
       const int t0 = tile_base + plan.v_tok[i];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        w[k] &= (t0 + 2 * k < L ? 0xFFFFu : 0u) | (t0 + 2 * k + 1 < L ? 0xFFFF0000u : 0u);
+        w[i][k] &= (t0 + 2 * k < L ? 0xFFFFu : 0u) | (t0 + 2 * k + 1 < L ? 0xFFFF0000u : 0u);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = bf16x2_to_f16x2(w[k]);
-    *reinterpret_cast<uint4*>(sV + plan.v_dst[i]) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+#pragma unroll
+  for (int i = 0; i < S::CH; ++i)
+    *reinterpret_cast<uint4*>(sV + plan.v_dst[i]) =
+        make_uint4(bf16x2_to_f16x2(w[i][0]), bf16x2_to_f16x2(w[i][1]), bf16x2_to_f16x2(w[i][2]),
+                   bf16x2_to_f16x2(w[i][3]));
 }
 
 // Row tile rt (rows [rt * R, rt * R + R) of the r = j * G + g order, R =
@@ -374,7 +383,10 @@ constexpr int kLdsNTW = 2;
 // prefix; most decodes read a few pages), and work-groups are dispatched in
 // index order, so sequences are listed by decreasing cost of their costliest
 // unit (longest processing time first): the long units start first and the
-// short ones fill in behind them.  A sequence's units stay contiguous, heaviest
+// short ones fill in behind them.  Prefill and decode units form two such
+// lists, merged in proportion to their lengths, so that the HBM-bound decodes
+// run beside the matrix-bound prefill tiles all through the launch rather
+// than after them.  A sequence's units stay contiguous, heaviest
 // first: its row tiles then run at the same time and stream the same K/V
 // pages, which they mostly find in L2 instead of each fetching the prefix from
 // HBM (work-group i goes to XCD i mod 8, so with Hkv a multiple of 8 all work-
@@ -382,89 +394,163 @@ constexpr int kLdsNTW = 2;
 // in tile steps of a work-group: a prefill row tile takes one step per 32-key
 // tile up to its last row's causal limit; a decode partition's tiles are
 // shared by the 4 waves.  One work-group of 1024 threads counts the units per
-// cost bucket in LDS, scans, and reserves a range per sequence (the order of
-// sequences within a bucket is arbitrary; each unit's result does not depend
-// on it).
+// cost bucket and list in LDS, scans, and reserves a range per sequence (the
+// order of sequences within a bucket is arbitrary; each unit's result does not
+// depend on it).
 // ---------------------------------------------------------------------------
 constexpr int kSchedThreads = 1024;
-constexpr int kCostBuckets = 4096;
+constexpr int kCostBuckets = 2048;
 
 __device__ __forceinline__ int unit_cost_bucket(int c) { return min(c, kCostBuckets - 1); }
 
-template <class F>
-__device__ __forceinline__ void for_each_unit(const ScheduleArgs& a, int b, F&& emit) {
+// Units of sequence b and the cost of its costliest unit, without walking
+// them: the last row tile reaches furthest, and the first decode partition
+// holds the extra tile of an uneven split.  Both are 0 for a sequence that
+// produces no work.
+__device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* units, int* cost) {
+  *units = 0;
+  *cost = 0;
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
-  if (q1 > a.num_tokens || q0 < 0 || q_len <= 0 || q_len > a.max_query_len) return;
+  if (q1 > a.num_tokens || q0 < 0 || q_len <= 0 || q_len > a.max_query_len) return false;
   const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
   if (q_len == 1) {
     const int Lp = min(L, a.max_partitions * a.partition_size);
     const int nparts = max(1, (Lp + a.partition_size - 1) / a.partition_size);
     const int tiles_all = (Lp + kTile - 1) / kTile;
-    const int per = tiles_all / nparts, extra = tiles_all % nparts;
-    for (int p = 0; p < nparts; ++p) {
-      const int t = per + (p < extra ? 1 : 0);
-      emit(b, -1 - p, (t + 3) / 4);
-    }
-    return;
+    const int first = tiles_all / nparts + (tiles_all % nparts ? 1 : 0);
+    *units = nparts;
+    *cost = (first + 3) / 4;
+    return true;
   }
   const int prior = L - q_len;
-  if (prior < 0) return;
-  const int G = a.group, R = a.rows_per_group;
-  const int n_rt = (q_len * G + R - 1) / R;
-  for (int rt = n_rt - 1; rt >= 0; --rt) {
-    const int hi = prior + min(q_len - 1, (rt * R + R - 1) / G);
-    emit(b, rt, hi / kTile + 1);
-  }
+  if (prior < 0) return false;
+  *units = (q_len * a.group + a.rows_per_group - 1) / a.rows_per_group;
+  *cost = (prior + q_len - 1) / kTile + 1;
+  return false;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
-  __shared__ int hist[kCostBuckets];
-  __shared__ int part[kSchedThreads];
-  for (int i = threadIdx.x; i < kCostBuckets; i += kSchedThreads) hist[i] = 0;
+// Exclusive prefix sum of one value per thread over the work-group (wave
+// scans, then a scan of the 16 wave totals); *total gets the sum of all.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
-  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
-    int nu = 0, cmax = 0;
-    for_each_unit(a, b, [&](int, int, int c) { ++nu; cmax = max(cmax, c); });
-    if (nu) atomicAdd(&hist[unit_cost_bucket(cmax)], nu);
+  if (w == 0) {
+    int t = lane < kSchedThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kSchedThreads / 64; off <<= 1) {
+      const int y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < kSchedThreads / 64) wsum[lane] = t;
   }
   __syncthreads();
-  // exclusive scan in decreasing cost: start[c] = number of units costlier than c
+  *total = wsum[kSchedThreads / 64 - 1];
+  const int base = w ? wsum[w - 1] : 0;
+  __syncthreads();
+  return base + x - v;
+}
+
+// Positions in the merged list of elements r, r + 1, ... of one list when the
+// prefill and decode lists (n_self and n_other elements) are interleaved in
+// proportion: element i of the prefill list sits at key (2i + 1) n_decode,
+// element j of the decode list at (2j + 1) n_prefill, prefill first on ties.
+// The count of other-list elements before element r is a quotient of
+// num(r) = (2r + 1) n_other - n_self by den = 2 n_self (ceiling for prefill,
+// floor + 1 for decode, clamped to [0, n_other]); it is kept as an exact
+// quotient and remainder and stepped by 2 n_other per element.
+struct MergeCursor {
+  long long q;                  // floor(num / den)
+  int rem, den, step_q, step_r, n_other, r;
+  bool decode;
+  __device__ __forceinline__ MergeCursor(int r0, int n_self, int n_oth, bool is_decode) {
+    den = 2 * n_self;
+    n_other = n_oth;
+    r = r0;
+    decode = is_decode;
+    const long long num = (2LL * r0 + 1) * n_oth - n_self;
+    // floor division of a possibly negative 64-bit value by a positive int
+    q = num >= 0 ? num / den : -((-num + den - 1) / den);
+    rem = (int)(num - q * den);
+    step_q = (2 * n_oth) / den;
+    step_r = (2 * n_oth) % den;
+  }
+  __device__ __forceinline__ int position() const {
+    long long before = decode ? (q >= 0 ? q + 1 : 0) : (q + (rem > 0 ? 1 : 0));
+    before = before < 0 ? 0 : (before > n_other ? n_other : before);
+    return r + (int)before;
+  }
+  __device__ __forceinline__ void next() {
+    ++r;
+    q += step_q;
+    rem += step_r;
+    if (rem >= den) {
+      rem -= den;
+      ++q;
+    }
+  }
+};
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
+  __shared__ int hist[2][kCostBuckets];      // [prefill, decode][cost bucket]
+  __shared__ int wsum[kSchedThreads / 64];
+  for (int i = threadIdx.x; i < 2 * kCostBuckets; i += kSchedThreads) hist[i / kCostBuckets][i % kCostBuckets] = 0;
+  __syncthreads();
+  // the summary of this thread's first sequence is kept for the second pass
+  int nu0 = 0, cmax0 = 0;
+  bool dec0 = false;
+  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
+    int nu, cmax;
+    const bool dec = seq_summary(a, b, &nu, &cmax);
+    if (b == threadIdx.x) {
+      nu0 = nu;
+      cmax0 = cmax;
+      dec0 = dec;
+    }
+    if (nu) atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu);
+  }
+  __syncthreads();
+  // exclusive scans in decreasing cost: start[c] = units of that list costlier than c
   constexpr int PER = kCostBuckets / kSchedThreads;
   const int top = kCostBuckets - 1 - PER * threadIdx.x;       // this thread's buckets: top, top-1, ...
-  int local[PER], sum = 0;
+  int n_list[2];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    local[i] = hist[top - i];
-    sum += local[i];
-  }
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += add;
-    __syncthreads();
-  }
-  const int total = part[kSchedThreads - 1];
-  int run = part[threadIdx.x] - sum;
+  for (int l = 0; l < 2; ++l) {
+    int local[PER], sum = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    hist[top - i] = run;
-    run += local[i];
+    for (int i = 0; i < PER; ++i) {
+      local[i] = hist[l][top - i];
+      sum += local[i];
+    }
+    int run = block_exclusive_scan(sum, &n_list[l], wsum);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      hist[l][top - i] = run;
+      run += local[i];
+    }
   }
   __syncthreads();
   for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
-    int nu = 0, cmax = 0;
-    for_each_unit(a, b, [&](int, int, int c) { ++nu; cmax = max(cmax, c); });
+    int nu = nu0, cmax = cmax0;
+    bool dec = dec0;
+    if (b != threadIdx.x) dec = seq_summary(a, b, &nu, &cmax);
     if (!nu) continue;
-    int pos = atomicAdd(&hist[unit_cost_bucket(cmax)], nu);    // a contiguous range for the sequence
-    for_each_unit(a, b, [&](int bb, int code, int) {
-      if (pos < a.unit_capacity) a.units[pos] = make_int2(bb, code);
-      ++pos;
-    });
+    // a contiguous range of its list; units heaviest first (the last row tile
+    // reaches furthest; decode partitions are in order)
+    MergeCursor cur(atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu), n_list[dec], n_list[!dec], dec);
+    for (int k = 0; k < nu; ++k, cur.next()) {
+      const int pos = cur.position();
+      if (pos < a.unit_capacity) a.units[pos] = make_int2(b, dec ? -1 - k : nu - 1 - k);
+    }
   }
-  if (threadIdx.x == 0) *a.unit_count = min(total, a.unit_capacity);
+  if (threadIdx.x == 0) *a.unit_count = min(n_list[0] + n_list[1], a.unit_capacity);
 }
 
 // ---------------------------------------------------------------------------

@@ -191,7 +191,8 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
  * P.V on fp16 matrix cores (P rounded to fp16, V converted from bf16):
  * precondition |V| < 65504, else results saturate.
  * fp32: a prefill kernel, then the decode of paged_gqa_decode (same meaning of
- * partition_size).
+ * partition_size).  bf16 batches with 2^20 or more work units (num_tokens * G /
+ * 128 + num_seqs * (1 + decode partitions)) return GQA_ERR_UNSUPPORTED.
  *
  * Workspace (device, >= chunked_prefill_paged_decode_workspace_size bytes for
  * the same dims, num_tokens, max_seq_len and partition_size; 256-byte
