@@ -256,6 +256,52 @@ def test_mixed_scale_sign(dtype, scale):
     assert_parity(got, ref, dtype, f"{bt.describe()} scale={scale}")
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_mixed_long_decodes_split_by_library(dtype):
+    """partition_size = 0 with decodes longer than the library's decode
+    partition: the long decodes are split and merged, the rest are not."""
+    q_lens = [1, 1, 37, 1, 1, 300]
+    seq_lens = [9000, 4100, 500, 4096, 17, 800]
+    bt = wl.make_batch(name="mlong", seed=61, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                       seq_lens=seq_lens, query_lens=q_lens, dtype=dtype, poison_slack=True)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale)
+    assert_parity(host(dev.mixed(0)), ref, dtype, bt.describe())
+
+
+def test_mixed_bf16_output_is_rounded_fp32():
+    """bf16 output of the mixed call is the fp32 result rounded to bf16."""
+    bt = wl.mixed_chunked(seed=4, num_seqs=24, token_budget=900)
+    dev = DeviceBatch(bt)
+    dev.cache_write()
+    o32 = dev.mixed(0, out_dtype=torch.float32)
+    o16 = dev.mixed(0, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert_parity(host(o16), oracle_after_write(bt, mixed=True), bt.dtype, bt.describe() + " bf16 out")
+
+
+def test_mixed_workspace_reuse_across_batches():
+    """One workspace serves successive mixed calls of different shapes: each
+    call's scheduling pass rewrites the unit list it reads."""
+    big = wl.mixed_chunked(seed=8, num_seqs=40, token_budget=1500)
+    small = wl.mixed_chunked(seed=9, num_seqs=12, token_budget=300)
+    dims = lambda bt, d: ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=d.key_cache,
+                                       block_tables=d.block_tables, q_dtype=d.query.dtype, out_dtype=torch.float32)
+    db, dsm = DeviceBatch(big), DeviceBatch(small)
+    nbytes = max(ops.mixed_workspace_size(dims(big, db), big.num_tokens, big.max_seq_len, 0),
+                 ops.mixed_workspace_size(dims(small, dsm), small.num_tokens, small.max_seq_len, 0))
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    for bt, d in ((big, db), (small, dsm), (big, db)):
+        d.cache_write()
+        out = ops.chunked_prefill_paged_decode(d.query, d.key_cache, d.value_cache, d.block_tables, d.seq_lens,
+                                               d.query_start_loc, bt.max_query_len, bt.max_seq_len, bt.scale,
+                                               workspace=ws)
+        assert_parity(host(out), oracle_after_write(bt, mixed=True), bt.dtype, bt.describe())
+
+
 def test_prefill_chunk_invariance_on_gpu():
     """A 96-token chunk equals three sequential 32-token chunks over the same cache."""
     L, C = 400, 96
