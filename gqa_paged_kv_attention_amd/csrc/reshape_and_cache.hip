@@ -17,17 +17,17 @@ constexpr int kThreads = 256;
 constexpr int kLdsSeqs = 4095;          // query_start_loc staged in LDS up to this many sequences
 
 // One thread per (token, kv head, 16-byte chunk of the head): VEC elements.
-// The work-group stages query_start_loc in LDS (one parallel load) so that
-// each thread finds its sequence by a binary search in LDS rather than a chain
-// of dependent global loads; beyond kLdsSeqs sequences it searches in memory.
+// The thread first guesses that token tok is the single new token of sequence
+// tok (a decode step): query_start_loc[tok], query_start_loc[tok + 1] and
+// seq_lens[tok] are loaded together with the source row, and only when the
+// guess fails does it search query_start_loc (staged in LDS by the work-group
+// when the batch is small enough, else in memory).  The work-group-wide
+// staging therefore sits behind a uniform branch that decode steps skip.
 template <int D, class T>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CH = D / VEC;
   __shared__ int s_qsl[kLdsSeqs + 1];
-  const bool staged = a.num_seqs <= kLdsSeqs;
-  if (staged)
-    for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) s_qsl[i] = a.query_start_loc[i];
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long per_tok = (long long)a.num_kv_heads * CH;
   const bool active = gid < (long long)a.num_tokens * per_tok;
@@ -41,21 +41,34 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
     kx = ld16(reinterpret_cast<const T*>(a.key) + src);
     vx = ld16(reinterpret_cast<const T*>(a.value) + src);
   }
-  __syncthreads();
-  if (!active) return;
-
-  // sequence owning this token: last b with query_start_loc[b] <= tok
-  int lo = 0, hi = a.num_seqs;           // invariant: qsl[lo] <= tok < qsl[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    const int v = staged ? s_qsl[mid] : a.query_start_loc[mid];
-    if (v <= tok) lo = mid; else hi = mid;
+  const int guess = min(tok, a.num_seqs - 1);
+  int q0 = a.query_start_loc[guess], q1 = a.query_start_loc[guess + 1];
+  int len = a.seq_lens[guess];
+  int b = guess;
+  const bool hit = q0 <= tok && tok < q1;
+  if (__syncthreads_and(hit || !active) == 0) {
+    // some token of the work-group is not in its guessed sequence: search
+    const bool staged = a.num_seqs <= kLdsSeqs;
+    if (staged)
+      for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) s_qsl[i] = a.query_start_loc[i];
+    __syncthreads();
+    if (active && !hit) {
+      // sequence owning this token: last b with query_start_loc[b] <= tok
+      int lo = 0, hi = a.num_seqs;           // invariant: qsl[lo] <= tok < qsl[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        const int v = staged ? s_qsl[mid] : a.query_start_loc[mid];
+        if (v <= tok) lo = mid; else hi = mid;
+      }
+      b = lo;
+      q0 = staged ? s_qsl[b] : a.query_start_loc[b];
+      q1 = staged ? s_qsl[b + 1] : a.query_start_loc[b + 1];
+      len = a.seq_lens[b];
+    }
   }
-  const int b = lo;
-  const int q0 = staged ? s_qsl[b] : a.query_start_loc[b];
-  const int q1 = staged ? s_qsl[b + 1] : a.query_start_loc[b + 1];
+  if (!active) return;
   if (tok < q0 || tok >= q1) return;
-  const int pos = a.seq_lens[b] - (q1 - q0) + (tok - q0);
+  const int pos = len - (q1 - q0) + (tok - q0);
   if (pos < 0 || pos >= a.max_blocks_per_seq * kPage) return;
   const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kPage];
   if ((unsigned)page >= (unsigned)a.num_blocks) return;

@@ -45,9 +45,13 @@ def mixed_step(bt, partition_size, out_dtype=torch.float32):
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("d", [64, 128])
-def test_reshape_and_cache_bit_exact(dtype, d):
+@pytest.mark.parametrize("kind", ["mixed", "decode", "one_chunk"])
+def test_reshape_and_cache_bit_exact(dtype, d, kind):
+    """Mixed batches take the query_start_loc search; a decode step (token t is
+    sequence t) and a single chunk hit the direct lookup."""
     rng = np.random.default_rng(7)
-    q_lens = np.array([1, 5, 0, 17, 1, 33, 2])
+    q_lens = {"mixed": np.array([1, 5, 0, 17, 1, 33, 2]), "decode": np.ones(300, dtype=np.int64),
+              "one_chunk": np.array([70])}[kind]
     seq_lens = q_lens + rng.integers(0, 40, size=len(q_lens))
     bt = wl.make_batch(name="rc", seed=8, num_heads=8, num_kv_heads=4, head_dim=d, block_size=16,
                        seq_lens=seq_lens, query_lens=q_lens, dtype=dtype)
