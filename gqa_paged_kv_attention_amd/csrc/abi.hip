@@ -113,13 +113,13 @@ long long mixed_unit_capacity(const gqa_dims& d, int32_t num_tokens, int nparts)
   return ((long long)num_tokens * G + rows - 1) / rows + (long long)d.num_seqs * (1 + nparts);
 }
 
-// Mixed-call workspace, bf16: [units, int2][unit count][decode partials].
+// Mixed-call workspace, bf16: [units, MixedUnit][unit count][decode partials].
 size_t mixed_bytes(const gqa_dims& d, int32_t num_tokens, int32_t max_seq_len, int32_t partition_size) {
   if (d.kv_dtype == GQA_F32) return decode_workspace(d, max_seq_len, partition_size);
   int psize = 0, nparts = 0;
   if (num_tokens < 0 || !mixed_decode_split(max_seq_len, partition_size, &psize, &nparts)) return 0;
   const long long cap = mixed_unit_capacity(d, num_tokens, nparts);
-  return align_up((size_t)cap * sizeof(int2)) + align_up(sizeof(int)) + partial_bytes(d, nparts);
+  return align_up((size_t)cap * sizeof(gqa::MixedUnit)) + align_up(sizeof(int)) + partial_bytes(d, nparts);
 }
 
 // Decode launch shared by paged_gqa_decode and the decode half of the mixed call.
@@ -357,8 +357,8 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
     const size_t need = mixed_bytes(dims, num_tokens, max_seq_len, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
     char* ws = reinterpret_cast<char*>(workspace);
-    int2* units = reinterpret_cast<int2*>(ws);
-    ws += align_up((size_t)cap * sizeof(int2));
+    gqa::MixedUnit* units = reinterpret_cast<gqa::MixedUnit*>(ws);
+    ws += align_up((size_t)cap * sizeof(gqa::MixedUnit));
     int* count = reinterpret_cast<int*>(ws);
     ws += align_up(sizeof(int));
     const size_t rows = (size_t)dims.num_seqs * dims.num_heads * nparts;

@@ -200,25 +200,21 @@ struct DecodeMergeLds {
   static constexpr int kFloats = kWaves * R * (2 + D + 4);
 };
 
-// Partition p of (sequence b, kv head kv), run by the 4 waves of a work-group;
-// `lds` holds DecodeMergeLds<D, NT>::kFloats floats.
+// Partition p of (sequence b, kv head kv), run by the 4 waves of a work-group,
+// for query row `row` and seq_lens[b] = seq_len; `lds` holds
+// DecodeMergeLds<D, NT>::kFloats floats.
 template <class Tile, int D, int NT, class OutT>
-__device__ __forceinline__ void decode_partition(const DecodeArgs& a, int p, int kv, int b, float* lds) {
+__device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, int kv, int b, int row, int seq_len,
+                                                    float* lds) {
   constexpr int R = NT * 16;            // padded rows of the group
   const int G = a.group;
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, q = lane >> 4;
 
-  int row = b;
-  if (a.query_start_loc) {
-    const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
-    if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
-    row = q0;
-  }
   typename Tile::Q qf[NT];
   load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
 
-  const int L = min(clamp_len(a.seq_lens[b], a.max_blocks_per_seq), a.max_partitions * a.partition_size);
+  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq), a.max_partitions * a.partition_size);
   const int nparts = (L + a.partition_size - 1) / a.partition_size;
   OutT* out = reinterpret_cast<OutT*>(a.out);
 
@@ -294,6 +290,19 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, int p, int
     for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
     a.partial_lse[(head0 + r) * a.max_partitions + p] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
   }
+}
+
+// As decode_partition_at, reading the query row (sequence b's only new token
+// when query_start_loc is given, else row b) and seq_lens[b] itself.
+template <class Tile, int D, int NT, class OutT>
+__device__ __forceinline__ void decode_partition(const DecodeArgs& a, int p, int kv, int b, float* lds) {
+  int row = b;
+  if (a.query_start_loc) {
+    const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+    if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
+    row = q0;
+  }
+  decode_partition_at<Tile, D, NT, OutT>(a, p, kv, b, row, a.seq_lens[b], lds);
 }
 
 }  // namespace

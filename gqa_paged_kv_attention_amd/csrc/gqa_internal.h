@@ -119,11 +119,17 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool 
 // decreasing cost; the fused kernel runs unit i / Hkv for kv head i % Hkv.
 // Rows of a prefill unit (depends only on the build):
 int prefill_lds_rows_per_group();
+// A scheduled unit: sequence b, code (>= 0: prefill row tile; < 0: decode
+// partition -1 - code), the sequence's query_start_loc[b], [b + 1] and
+// seq_lens[b], so that the unit's work-group reads them with the unit.
+struct MixedUnit {
+  int4 a;                           // {b, code, q0, q1}
+  int4 b;                           // {seq_len, 0, 0, 0}
+};
 struct ScheduleArgs {
   const int32_t* seq_lens;
   const int32_t* query_start_loc;
-  int2* units;                      // [unit_capacity] {sequence, code}: code >= 0 prefill row tile,
-                                    // code < 0 decode partition -1 - code
+  MixedUnit* units;                 // [unit_capacity]
   int* unit_count;
   int unit_capacity;
   int num_seqs;
@@ -138,7 +144,7 @@ struct ScheduleArgs {
 struct MixedArgs {
   PrefillArgs prefill;
   DecodeArgs decode;
-  const int2* units;
+  const MixedUnit* units;
   const int* unit_count;
 };
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream);

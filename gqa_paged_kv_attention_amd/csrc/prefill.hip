@@ -146,16 +146,17 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 }
 
 // Row tile rt (rows [rt * R, rt * R + R) of the r = j * G + g order, R =
-// kRowsPerGroup) of sequence b against kv head kv.  sK / sV: two LDS buffers
+// kRowsPerGroup) of sequence b (new tokens [q0, q1), seq_lens[b] = seq_len)
+// against kv head kv.  sK / sV: two LDS buffers
 // of KBUF and VBUF elements each.
 template <int D, int NTW, class OutT>
-__device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int kv, uint16_t* sK, uint16_t* sV) {
+__device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int q0, int q1, int seq_len, int kv,
+                                             uint16_t* sK, uint16_t* sV) {
   typedef PrefillLds<D, NTW> S;
   const int G = a.group;
-  const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0) return;
-  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
+  const int L = max(0, min(seq_len, a.max_blocks_per_seq * kPage));
   const int prior = L - q_len;
   if (prior < 0) return;
   const int rows_total = q_len * G;
@@ -407,13 +408,19 @@ __device__ __forceinline__ int unit_cost_bucket(int c) { return min(c, kCostBuck
 // them: the last row tile reaches furthest, and the first decode partition
 // holds the extra tile of an uneven split.  Both are 0 for a sequence that
 // produces no work.
-__device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* units, int* cost) {
+struct SeqInfo {
+  int q0, q1, seq_len;
+};
+
+__device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* units, int* cost, SeqInfo* info) {
   *units = 0;
   *cost = 0;
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+  const int sl = a.seq_lens[b];
+  *info = SeqInfo{q0, q1, sl};
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0 || q_len <= 0 || q_len > a.max_query_len) return false;
-  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
+  const int L = max(0, min(sl, a.max_blocks_per_seq * kPage));
   if (q_len == 1) {
     const int Lp = min(L, a.max_partitions * a.partition_size);
     const int nparts = max(1, (Lp + a.partition_size - 1) / a.partition_size);
@@ -506,13 +513,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   // the summary of this thread's first sequence is kept for the second pass
   int nu0 = 0, cmax0 = 0;
   bool dec0 = false;
+  SeqInfo info0{0, 0, 0};
   for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
     int nu, cmax;
-    const bool dec = seq_summary(a, b, &nu, &cmax);
+    SeqInfo info;
+    const bool dec = seq_summary(a, b, &nu, &cmax, &info);
     if (b == threadIdx.x) {
       nu0 = nu;
       cmax0 = cmax;
       dec0 = dec;
+      info0 = info;
     }
     if (nu) atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu);
   }
@@ -540,14 +550,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
     int nu = nu0, cmax = cmax0;
     bool dec = dec0;
-    if (b != threadIdx.x) dec = seq_summary(a, b, &nu, &cmax);
+    SeqInfo info = info0;
+    if (b != threadIdx.x) dec = seq_summary(a, b, &nu, &cmax, &info);
     if (!nu) continue;
     // a contiguous range of its list; units heaviest first (the last row tile
     // reaches furthest; decode partitions are in order)
     MergeCursor cur(atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu), n_list[dec], n_list[!dec], dec);
     for (int k = 0; k < nu; ++k, cur.next()) {
       const int pos = cur.position();
-      if (pos < a.unit_capacity) a.units[pos] = make_int2(b, dec ? -1 - k : nu - 1 - k);
+      if (pos < a.unit_capacity) {
+        a.units[pos].a = make_int4(b, dec ? -1 - k : nu - 1 - k, info.q0, info.q1);
+        a.units[pos].b = make_int4(info.seq_len, 0, 0, 0);
+      }
     }
   }
   if (threadIdx.x == 0) *a.unit_count = min(n_list[0] + n_list[1], a.unit_capacity);
@@ -576,13 +590,17 @@ void mixed_kernel(MixedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[MixedLds<D, NT>::kBytes];
   const int Hkv = a.prefill.num_kv_heads;
   const int slot = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
-  if (slot >= *a.unit_count) return;
-  const int2 u = a.units[slot];
+  // the record is read together with the count (slot < the list's capacity)
+  const int count = *a.unit_count;
+  const int4 u = a.units[slot].a;
+  const int seq_len = a.units[slot].b.x;
+  if (slot >= count) return;
   if (u.y >= 0) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, kv, sK, sK + 2 * S::KBUF);
+    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, u.z, u.w, seq_len, kv, sK, sK + 2 * S::KBUF);
   } else {
-    decode_partition<TileBF16<D>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, reinterpret_cast<float*>(lds));
+    decode_partition_at<TileBF16<D>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, seq_len,
+                                                  reinterpret_cast<float*>(lds));
   }
 }
 
