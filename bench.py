@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-gqa-comparison", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -114,6 +115,49 @@ def cpu_baseline(bt, seconds):
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_seq} sequence decodes ({n_seq / bt.num_seqs:.2f} passes over the {bt.num_seqs}-sequence "
                       f"batch), numpy fp64 with BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def gqa_comparison(dev, stream, reps):
+    """The GQA saving at kernel level, on the Llama-2-7B decode sweep shape (128
+    sequences, Hq=32, d=128, context U{32..1024}).  The GQA batch (Hkv=8) is timed
+    as it is and with its K/V expanded per query head (Hkv=32, the cache an
+    MHA-style kernel reads; outputs must agree), and an MQA batch (Hkv=1) with
+    the same lengths."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    def run(bt, kc, vc):
+        q, tb, sl = ops.to_device(bt.query, dev), ops.to_device(bt.block_tables, dev), ops.to_device(bt.seq_lens, dev)
+        out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tb,
+                             q_dtype=q.dtype, out_dtype=out.dtype)
+        ws = torch.zeros(max(ops.decode_workspace_size(dims, bt.max_seq_len, 0), 1), dtype=torch.uint8, device=dev)
+        f = lambda: ops.paged_gqa_decode(q, kc, vc, tb, sl, bt.max_seq_len, bt.scale, out=out, workspace=ws)
+        for _ in range(3):
+            f()
+        ms = event_time_ms(f, reps, stream)
+        return ms, out.clone()
+
+    gqa = wl.llama2_7b_sweep(8, seed=3)
+    kc, vc = ops.to_device(gqa.key_cache, dev), ops.to_device(gqa.value_cache, dev)
+    t_gqa, o_gqa = run(gqa, kc, vc)
+    G = gqa.num_heads // gqa.num_kv_heads
+    kce, vce = kc.repeat_interleave(G, dim=1).contiguous(), vc.repeat_interleave(G, dim=1).contiguous()
+    del kc, vc
+    t_exp, o_exp = run(gqa, kce, vce)
+    del kce, vce
+    mqa = wl.llama2_7b_sweep(1, seed=3)
+    t_mqa, _ = run(mqa, ops.to_device(mqa.key_cache, dev), ops.to_device(mqa.value_cache, dev))
+    torch.cuda.synchronize()
+    tokens = int(gqa.seq_lens.sum())
+    per_tok = 2 * gqa.head_dim * 2
+    return {"workload": "llama2_7b_sweep (128 seqs, Hq=32, d=128, context U{32..1024}, bf16)",
+            "expanded_kv_us": round(t_exp * 1e3, 2), "gqa_us": round(t_gqa * 1e3, 2), "mqa_us": round(t_mqa * 1e3, 2),
+            "kv_bytes": {"expanded": tokens * per_tok * gqa.num_heads, "gqa": tokens * per_tok * gqa.num_kv_heads,
+                         "mqa": tokens * per_tok},
+            "expanded_over_gqa": round(t_exp / t_gqa, 3),
+            "max_abs_diff_expanded_vs_gqa": float((o_exp - o_gqa).abs().max())}
 
 
 def main():
@@ -220,6 +264,9 @@ def main():
                                  "algorithmic_gflop": round(flops / 1e9, 3),
                                  "mfma_util": round(flops / (mixed_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
                                  "kv_gb": round(mb.kv_bytes() / 1e9, 4)}
+
+    if not args.no_gqa_comparison:
+        record["gqa_comparison"] = gqa_comparison(dev, stream, 30)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)

@@ -306,6 +306,51 @@ def test_mixed_workspace_reuse_across_batches():
         assert_parity(host(out), oracle_after_write(bt, mixed=True), bt.dtype, bt.describe())
 
 
+@pytest.mark.parametrize("mode", ["decode0", "decode512", "mixed"])
+def test_prefix_shared_pages(mode):
+    """Sequences whose block tables alias the pages of a shared prompt prefix
+    (read-only sharing, new tokens in private pages)."""
+    rng = np.random.default_rng(71)
+    B, prefix_pages = 12, 64                       # 1024 shared tokens
+    if mode == "mixed":
+        q_lens = [1, 40, 1, 1, 130, 1, 7, 1, 1, 64, 1, 2]
+    else:
+        q_lens = [1] * B
+    seq_lens = [prefix_pages * 16 + int(x) + q for x, q in zip(rng.integers(1, 600, size=B), q_lens)]
+    bt = wl.make_batch(name="prefix", seed=72, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       seq_lens=seq_lens, query_lens=q_lens, dtype=wl.BF16)
+    for b in range(1, B):
+        bt.block_tables[b, :prefix_pages] = bt.block_tables[0, :prefix_pages]
+    dev = DeviceBatch(bt)
+    dev.cache_write()
+    kc, vc = cache_write_ref(bt.new_key, bt.new_value, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                             bt.query_start_loc)
+    if mode == "mixed":
+        ref = paged_attention_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.query_start_loc,
+                                  bt.num_kv_heads, bt.scale)
+        got = host(dev.mixed(0))
+    else:
+        ref = decode_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.num_kv_heads, bt.scale)
+        got = host(dev.decode(0 if mode == "decode0" else 512))
+    assert_parity(got, ref, bt.dtype, f"{bt.describe()} {mode}")
+
+
+def test_gqa_equals_expanded_kv_on_gpu():
+    """The grouped decode equals the same decode over K/V expanded per query
+    head (Hkv = Hq), the layout a GQA-unaware kernel reads."""
+    bt = wl.llama2_7b_sweep(8, seed=3, num_seqs=24)
+    dev = DeviceBatch(bt)
+    G = bt.num_heads // bt.num_kv_heads
+    grouped = host(dev.decode(0))
+    kce = dev.key_cache.repeat_interleave(G, dim=1).contiguous()
+    vce = dev.value_cache.repeat_interleave(G, dim=1).contiguous()
+    expanded = host(ops.paged_gqa_decode(dev.query, kce, vce, dev.block_tables, dev.seq_lens, bt.max_seq_len,
+                                         bt.scale))
+    assert np.max(np.abs(expanded - grouped)) <= 1e-5
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads, bt.scale)
+    assert_parity(grouped, ref, bt.dtype, bt.describe())
+
+
 def test_prefill_chunk_invariance_on_gpu():
     """A 96-token chunk equals three sequential 32-token chunks over the same cache."""
     L, C = 400, 96

@@ -194,6 +194,27 @@ def test_page_permutation_invariance():
     assert np.array_equal(run_ref(bt2), ref)
 
 
+def test_prefix_shared_pages_equal_duplicated_pages():
+    """Block tables may alias physical pages (a shared prompt prefix): the result
+    equals that of the same batch with the shared pages copied into private
+    ones."""
+    seq_lens, q_lens = [37, 29, 44], [3, 1, 2]
+    bt = small_batch(24, seq_lens, q_lens, Hq=4, Hkv=2, d=8, bs=4)
+    shared = 5                                     # first 5 pages (20 tokens) of sequence 0
+    aliased = small_batch(24, seq_lens, q_lens, Hq=4, Hkv=2, d=8, bs=4)
+    for b in (1, 2):
+        aliased.block_tables[b, :shared] = aliased.block_tables[0, :shared]
+    # duplicated: copy sequence 0's prefix pages into each sequence's own pages
+    dup = small_batch(24, seq_lens, q_lens, Hq=4, Hkv=2, d=8, bs=4)
+    for b in (1, 2):
+        own = dup.block_tables[b, :shared]
+        src = dup.block_tables[0, :shared]
+        dup.key_cache[own] = dup.key_cache[src]
+        dup.value_cache[own] = dup.value_cache[src]
+    assert np.array_equal(run_ref(aliased), run_ref(dup))
+    assert not np.array_equal(run_ref(aliased), run_ref(bt))      # the prefix really changed
+
+
 def test_nan_poison_outside_sequences_is_ignored():
     seq_lens, q_lens = [13, 6, 32], [2, 1, 5]
     clean = small_batch(23, seq_lens, q_lens, bs=8)
