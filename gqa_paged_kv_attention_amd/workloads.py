@@ -177,20 +177,24 @@ def make_batch(*, name: str, seed: int, num_heads: int, num_kv_heads: int, head_
                block_size: int, seq_lens: Sequence[int], query_lens: Sequence[int], dtype: str,
                scale: Optional[float] = None, slack_frac: float = 0.1,
                max_blocks_per_seq: Optional[int] = None, poison_slack: bool = False,
-               rng: Optional[np.random.Generator] = None) -> PagedBatch:
+               rng: Optional[np.random.Generator] = None, cross: bool = False) -> PagedBatch:
     """Build a batch: a seeded permutation of physical pages and N(0,1) data.
 
     Every page of the pool (including slack pages that no sequence owns) is
     filled with N(0,1) values; ``poison_slack`` fills the slack pages with NaN
     instead, so that an out-of-table read shows up in the output.  Block-table
-    entries past a sequence's last page point at a slack page.
+    entries past a sequence's last page point at a slack page.  ``cross``
+    marks a cross-attention batch: ``seq_lens`` are encoder lengths and a
+    sequence may have more query rows than encoder positions.
     """
     rng = rng if rng is not None else np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     query_lens = np.asarray(query_lens, dtype=np.int32)
     if seq_lens.shape != query_lens.shape:
         raise ValueError("seq_lens and query_lens differ in length")
-    if (query_lens > seq_lens).any() or (query_lens < 0).any():
+    if (query_lens < 0).any() or (seq_lens < 0).any():
+        raise ValueError("lengths must be non-negative")
+    if not cross and (query_lens > seq_lens).any():
         raise ValueError("each query length must lie in [0, seq_len]")
     B = int(seq_lens.shape[0])
     pages = (seq_lens.astype(np.int64) + block_size - 1) // block_size
@@ -306,6 +310,18 @@ def longctx_splitk(seed: int = 5, num_seqs: int = 16, ctx: int = 32768, **kw) ->
     return make_batch(name="longctx_splitk", seed=seed, num_heads=64, num_kv_heads=8, head_dim=128,
                       block_size=16, seq_lens=np.full(num_seqs, ctx, np.int32),
                       query_lens=np.ones(num_seqs, np.int32), dtype=BF16, rng=rng, **kw)
+
+
+def cross_attention(seed: int = 6, num_seqs: int = 16, enc_lo: int = 1024, enc_hi: int = 6400,
+                    query_len: int = 1, **kw) -> PagedBatch:
+    """Cross-attention over a static encoder cache: ``query_len`` decoder rows
+    per sequence against U{enc_lo..enc_hi} encoder positions; 16 sequences,
+    Hq=32, Hkv=8, d=128, block 16, bf16."""
+    rng = np.random.default_rng(seed)
+    enc = rng.integers(enc_lo, enc_hi + 1, size=num_seqs)
+    return make_batch(name=f"cross_attention_q{query_len}", seed=seed, num_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, seq_lens=enc,
+                      query_lens=np.full(num_seqs, query_len, np.int32), dtype=BF16, rng=rng, cross=True, **kw)
 
 
 LONGCTX_PARTITION = 512

@@ -25,6 +25,13 @@ What it computes, written as the plain definition (slow, vectorised per
   of ``q_len`` new tokens is the *last* ``q_len`` tokens of the sequence (the
   cache already holds them), and new token ``j`` sees key positions
   ``t <= seq_len - q_len + j`` (causal, bottom-right aligned).
+* Cross-attention over a static encoder cache ("[Core] More-efficient
+  cross-attention parallel QKV computation", vLLM PR #7448, opening post: the
+  decoder supplies the queries, the encoder output supplies keys and values,
+  and after prefill only queries are new).  Reading where the page is silent:
+  no causal mask, so every query row of sequence ``b`` sees all
+  ``seq_lens[b]`` encoder positions, a chunk may be longer than the encoder
+  sequence, and an empty encoder sequence gives zero rows (``causal=False``).
 * Split-K: partition ``p`` of a decode covers keys ``[p*P, min((p+1)*P, L))`` and
   yields the normalised partial output and its natural-log log-sum-exp; merging
   partials weighted by ``exp(lse_p - logsumexp(lse))`` gives the unsplit result.
@@ -71,13 +78,15 @@ def _softmax_rows(S: np.ndarray) -> np.ndarray:
 
 
 def paged_attention_ref(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
-                        num_kv_heads: int, scale: float, seqs=None, return_weights: bool = False):
+                        num_kv_heads: int, scale: float, seqs=None, return_weights: bool = False,
+                        causal: bool = True):
     """Attention of a mixed batch (prefill chunks and decodes) over the paged cache.
 
     ``query``: ``[T, Hq, d]``.  Returns ``out [T, Hq, d]`` float64 (rows of
     sequences not listed in ``seqs`` stay zero).  With ``return_weights`` also
     returns ``{b: W}``, the softmax weights of sequence ``b`` shaped
-    ``[q_len, Hq, seq_len]``.
+    ``[q_len, Hq, seq_len]``.  ``causal=False`` is cross-attention: every row
+    sees all ``seq_len`` keys.
     """
     Q = _to_f64(query)
     T, Hq, d = Q.shape
@@ -95,13 +104,20 @@ def paged_attention_ref(query, key_cache, value_cache, block_tables, seq_lens, q
         q_len = q1 - q0
         if q_len == 0:
             continue
-        if q_len > L:
-            raise ValueError(f"sequence {b}: query length {q_len} exceeds seq_len {L}")
-        prior = L - q_len
-        # key t is visible to new token j iff t <= prior + j
-        visible = np.arange(L)[None, :] <= (prior + np.arange(q_len))[:, None]       # [q_len, L]
+        if causal:
+            if q_len > L:
+                raise ValueError(f"sequence {b}: query length {q_len} exceeds seq_len {L}")
+            # key t is visible to new token j iff t <= (L - q_len) + j
+            visible = np.arange(L)[None, :] <= (L - q_len + np.arange(q_len))[:, None]   # [q_len, L]
+        else:
+            visible = np.ones((q_len, L), dtype=bool)
         if return_weights:
             W_b = np.zeros((q_len, Hq, L))
+        if L == 0:
+            # no visible key: the rows stay zero
+            if return_weights:
+                weights[b] = W_b
+            continue
         for kv in range(num_kv_heads):
             K, V = gather_sequence(key_cache, value_cache, block_tables[b], L, kv)
             Qg = Q[q0:q1, kv * G:(kv + 1) * G, :]                                     # [q_len, G, d]

@@ -35,8 +35,9 @@ def run_ref(bt, **kw):
                                bt.query_start_loc, bt.num_kv_heads, bt.scale, **kw)
 
 
-def bruteforce(bt):
-    """Pure-Python loops: per token, per head, per key, with math.exp."""
+def bruteforce(bt, causal=True):
+    """Pure-Python loops: per token, per head, per key, with math.exp.  A row
+    with no visible key stays zero."""
     Hq, Hkv, d, bs = bt.num_heads, bt.num_kv_heads, bt.head_dim, bt.block_size
     G = Hq // Hkv
     Kc, Vc, Q = f(bt.key_cache), f(bt.value_cache), f(bt.query)
@@ -45,7 +46,9 @@ def bruteforce(bt):
         L = int(bt.seq_lens[b])
         q0, q1 = int(bt.query_start_loc[b]), int(bt.query_start_loc[b + 1])
         for j in range(q1 - q0):
-            last_visible = L - (q1 - q0) + j
+            last_visible = L - (q1 - q0) + j if causal else L - 1
+            if last_visible < 0:
+                continue
             for h in range(Hq):
                 kv = h // G
                 scores = []
@@ -101,6 +104,81 @@ def test_bruteforce_mixed(seed):
 def test_bruteforce_bf16_mqa():
     bt = small_batch(7, [9, 17, 1], [1, 3, 1], Hq=4, Hkv=1, d=8, bs=4, dtype=wl.BF16)
     assert np.max(np.abs(run_ref(bt) - bruteforce(bt))) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# cross-attention (no causal mask) over a static encoder cache
+# --------------------------------------------------------------------------
+
+def cross_batch(seed, enc_lens, q_lens, **kw):
+    return small_batch(seed, enc_lens, q_lens, cross=True, **kw)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_cross_bruteforce(seed):
+    # chunks longer than, equal to and shorter than the encoder sequence, a
+    # single-row decode, an empty encoder and an empty chunk
+    bt = cross_batch(40 + seed, [9, 5, 23, 0, 14], [12, 5, 3, 2, 0], Hq=6, Hkv=2, d=5, bs=4)
+    ref = run_ref(bt, causal=False)
+    assert np.max(np.abs(ref - bruteforce(bt, causal=False))) <= 1e-12
+    q0, q1 = bt.query_start_loc[3], bt.query_start_loc[4]
+    assert not ref[q0:q1].any()                    # empty encoder: zero rows
+
+
+def test_cross_bruteforce_bf16_mqa():
+    bt = cross_batch(42, [7, 17], [9, 1], Hq=4, Hkv=1, d=8, bs=4, dtype=wl.BF16)
+    assert np.max(np.abs(run_ref(bt, causal=False) - bruteforce(bt, causal=False))) <= 1e-12
+
+
+def test_cross_equals_unmasked_sdpa():
+    """Library cross-check: torch SDPA in float64 without a mask, K/V expanded per query head."""
+    bt = cross_batch(43, [21, 40, 3], [30, 1, 6], Hq=8, Hkv=2, d=16, bs=8, dtype=wl.BF16)
+    G = bt.num_heads // bt.num_kv_heads
+    Q = torch.from_numpy(f(bt.query))
+    want = torch.zeros(bt.num_tokens, bt.num_heads, bt.head_dim, dtype=torch.float64)
+    for b in range(bt.num_seqs):
+        L = int(bt.seq_lens[b])
+        q0, q1 = int(bt.query_start_loc[b]), int(bt.query_start_loc[b + 1])
+        kv = [gather_sequence(bt.key_cache, bt.value_cache, bt.block_tables[b], L, h) for h in range(2)]
+        K = torch.stack([torch.from_numpy(k) for k, _ in kv]).repeat_interleave(G, dim=0)
+        V = torch.stack([torch.from_numpy(v) for _, v in kv]).repeat_interleave(G, dim=0)
+        q = Q[q0:q1].transpose(0, 1).contiguous()
+        o = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=bt.scale)
+        want[q0:q1] = o.transpose(0, 1)
+    assert np.max(np.abs(run_ref(bt, causal=False) - want.numpy())) <= 1e-10
+
+
+def test_cross_zero_scale_gives_mean_of_all_encoder_values():
+    """Every row (not a causal prefix) averages all encoder positions."""
+    bt = cross_batch(44, [11, 6], [4, 9], Hq=4, Hkv=2, d=4, bs=4)
+    bt.scale = 0.0
+    out = run_ref(bt, causal=False)
+    Vc = f(bt.value_cache)
+    for b in range(2):
+        L = int(bt.seq_lens[b])
+        q0, q1 = int(bt.query_start_loc[b]), int(bt.query_start_loc[b + 1])
+        for h in range(4):
+            vals = [Vc[bt.block_tables[b][t // 4], h // 2, :, t % 4] for t in range(L)]
+            np.testing.assert_allclose(out[q0:q1, h], np.broadcast_to(np.mean(vals, axis=0), (q1 - q0, 4)),
+                                       rtol=0, atol=1e-13)
+
+
+def test_cross_rows_are_independent_of_position():
+    """Reversing a chunk's query rows reverses its output rows; each row equals
+    the decode of that row alone."""
+    bt = cross_batch(45, [19], [7], Hq=4, Hkv=2, d=8, bs=4)
+    out = run_ref(bt, causal=False)
+    rev = cross_batch(45, [19], [7], Hq=4, Hkv=2, d=8, bs=4)
+    rev.query = bt.query[::-1].copy()
+    np.testing.assert_array_equal(run_ref(rev, causal=False), out[::-1])
+    for j in range(7):
+        one = decode_ref(bt.query[j:j + 1], bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                         bt.num_kv_heads, bt.scale)
+        np.testing.assert_allclose(out[j], one[0], rtol=0, atol=1e-13)
+    # the causal reading differs on every row but the last
+    causal = run_ref(bt)
+    assert all(not np.allclose(out[j], causal[j]) for j in range(6))
+    np.testing.assert_allclose(out[6], causal[6], rtol=0, atol=1e-13)
 
 
 # --------------------------------------------------------------------------
