@@ -8,8 +8,10 @@ randomly permuted pages, seeded synthetic N(0,1) data.
 
 Metric: effective KV GB/s = sum(seq_len) * 2 * Hkv * d * 2 bytes / step time.
 Also reported: the decode kernel's roofline (HIP events on its launch
-stream), the mixed chunked-prefill + decode batch's tokens/s, and the CPU
-oracle's throughput on a bounded sample as a baseline.
+stream), the mixed chunked-prefill + decode batch's tokens/s, the GQA saving
+against the same cache expanded per query head, cross-attention over a static
+encoder cache, and the CPU oracle's throughput on a bounded sample as a
+baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
        python bench.py --copy-calibration   (a plain 512 MiB device copy, for
@@ -37,7 +39,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "c5298fc22e8185bed58bb26c1d175694d6ce20a3a4af98ef6f046fa7b63f6f41", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 649356021, "write_bytes_per_call": 6336680, "hbm_bytes_per_call": 655692701, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "e00a7813afbd4c5e94d1c6ca0e425841763649f63881043d5001778fa9c2a57c", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 649567028, "write_bytes_per_call": 6337586, "hbm_bytes_per_call": 655904614, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
@@ -51,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-gqa-comparison", action="store_true")
+    ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -160,6 +163,45 @@ def gqa_comparison(dev, stream, reps):
             "max_abs_diff_expanded_vs_gqa": float((o_exp - o_gqa).abs().max())}
 
 
+def cross_attention_leg(dev, stream, reps):
+    """Cross-attention over a static encoder cache (16 sequences, Hq=32, Hkv=8,
+    d=128, bf16, encoder lengths U{1024..6400}): a decode step (one decoder row
+    per sequence, HBM-bound) and a chunk of 256 decoder rows per sequence
+    (matrix-bound).  No cache write: the encoder cache is static."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    res = {"workload": "cross_attention (16 seqs, Hq=32, Hkv=8, d=128, encoder U{1024..6400}, bf16)"}
+    for q_len in (1, 256):
+        bt = wl.cross_attention(seed=6, query_len=q_len)
+        up = lambda a: ops.to_device(a, dev)
+        q, kc, vc = up(bt.query), up(bt.key_cache), up(bt.value_cache)
+        tb, el, qsl = up(bt.block_tables), up(bt.seq_lens), up(bt.query_start_loc)
+        out = torch.empty(bt.num_tokens, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tb,
+                             q_dtype=q.dtype, out_dtype=out.dtype)
+        ws = torch.zeros(max(ops.cross_workspace_size(dims, bt.num_tokens, bt.max_seq_len, 0), 1),
+                         dtype=torch.uint8, device=dev)
+        f = lambda: ops.paged_cross_attention(q, kc, vc, tb, el, qsl, bt.max_query_len, bt.max_seq_len, bt.scale,
+                                              out=out, workspace=ws)
+        for _ in range(3):
+            f()
+        ms = event_time_ms(f, reps, stream)
+        enc = bt.seq_lens.astype(np.int64)
+        if q_len == 1:
+            gbs = bt.kv_bytes() / (ms * 1e-3) / 1e9
+            res["decode_step"] = {"us": round(ms * 1e3, 2), "kv_bytes": bt.kv_bytes(), "kv_gbs": round(gbs, 1),
+                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            flops = 4 * bt.head_dim * bt.num_heads * int(np.sum(enc * q_len))
+            res[f"chunk_{q_len}"] = {"us": round(ms * 1e3, 2), "gflop": round(flops / 1e9, 3),
+                                     "tokens_per_s": round(bt.num_tokens / (ms * 1e-3), 1),
+                                     "mfma_util": round(flops / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
+        del q, kc, vc, out, ws
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -267,6 +309,9 @@ def main():
 
     if not args.no_gqa_comparison:
         record["gqa_comparison"] = gqa_comparison(dev, stream, 30)
+
+    if not args.no_cross:
+        record["cross_attention"] = cross_attention_leg(dev, stream, 30)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)

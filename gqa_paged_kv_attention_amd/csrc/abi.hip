@@ -113,13 +113,17 @@ long long mixed_unit_capacity(const gqa_dims& d, int32_t num_tokens, int nparts)
   return ((long long)num_tokens * G + rows - 1) / rows + (long long)d.num_seqs * (1 + nparts);
 }
 
-// Mixed-call workspace, bf16: [units, MixedUnit][unit count][decode partials].
+// Mixed-call workspace, bf16: [units, MixedUnit][unit count][decode partials],
+// or the decode's workspace if larger (a batch of decodes only runs the decode).
 size_t mixed_bytes(const gqa_dims& d, int32_t num_tokens, int32_t max_seq_len, int32_t partition_size) {
-  if (d.kv_dtype == GQA_F32) return decode_workspace(d, max_seq_len, partition_size);
+  const size_t dec = decode_workspace(d, max_seq_len, partition_size);
+  if (d.kv_dtype == GQA_F32) return dec;
   int psize = 0, nparts = 0;
   if (num_tokens < 0 || !mixed_decode_split(max_seq_len, partition_size, &psize, &nparts)) return 0;
   const long long cap = mixed_unit_capacity(d, num_tokens, nparts);
-  return align_up((size_t)cap * sizeof(gqa::MixedUnit)) + align_up(sizeof(int)) + partial_bytes(d, nparts);
+  const size_t fused =
+      align_up((size_t)cap * sizeof(gqa::MixedUnit)) + align_up(sizeof(int)) + partial_bytes(d, nparts);
+  return std::max(fused, dec);
 }
 
 // Decode launch shared by paged_gqa_decode and the decode half of the mixed call.
@@ -212,6 +216,149 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   r.num_tokens = num_tokens;
   r.skip_single = 1;
   return status_from(gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, stream));
+}
+
+// Mixed batch of prefill chunks and decodes; `causal` false is cross-attention
+// (every row sees all seq_len keys, and a chunk may be longer than seq_len).
+int run_mixed(void* out, const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
+              int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, const gqa_dims& dims, float scale,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t s, bool causal) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || num_tokens < 0 || max_query_len < 0) return GQA_ERR_INVALID_ARG;
+  if (causal && max_query_len > max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs == 0 || num_tokens == 0) {
+    int ps = 0, np = 0;
+    return partitioning(max_seq_len, partition_size, &ps, &np) ? GQA_OK : GQA_ERR_INVALID_ARG;
+  }
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc)
+    return GQA_ERR_INVALID_ARG;
+  // decodes only: the decode launch (one query row sees every key either way)
+  if (max_query_len <= 1)
+    return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
+                      max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
+  const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
+  const int G = dims.num_heads / dims.num_kv_heads;
+  const float scale_log2 = scale * 1.4426950408889634f;
+
+  gqa::PrefillArgs p;
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.query_start_loc = query_start_loc;
+  p.num_seqs = dims.num_seqs;
+  p.num_heads = dims.num_heads;
+  p.num_kv_heads = dims.num_kv_heads;
+  p.group = G;
+  p.num_blocks = dims.num_blocks;
+  p.max_blocks_per_seq = dims.max_blocks_per_seq;
+  p.num_tokens = num_tokens;
+  p.scale_log2 = scale_log2;
+  p.causal = causal ? 1 : 0;
+
+  if (!kv_f32) {
+    // scheduling pass + fused prefill/decode kernel (+ merge of split decodes)
+    int psize = 0, nparts = 0;
+    if (!mixed_decode_split(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
+    const long long cap = mixed_unit_capacity(dims, num_tokens, nparts);
+    if (cap >= kMaxMixedUnits || cap * dims.num_kv_heads > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    const size_t need = mixed_bytes(dims, num_tokens, max_seq_len, partition_size);
+    if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    char* ws = reinterpret_cast<char*>(workspace);
+    gqa::MixedUnit* units = reinterpret_cast<gqa::MixedUnit*>(ws);
+    ws += align_up((size_t)cap * sizeof(gqa::MixedUnit));
+    int* count = reinterpret_cast<int*>(ws);
+    ws += align_up(sizeof(int));
+    const size_t rows = (size_t)dims.num_seqs * dims.num_heads * nparts;
+
+    gqa::ScheduleArgs sa;
+    sa.seq_lens = seq_lens;
+    sa.query_start_loc = query_start_loc;
+    sa.units = units;
+    sa.unit_count = count;
+    sa.unit_capacity = (int)cap;
+    sa.num_seqs = dims.num_seqs;
+    sa.num_tokens = num_tokens;
+    sa.max_query_len = max_query_len;
+    sa.group = G;
+    sa.rows_per_group = gqa::prefill_lds_rows_per_group();
+    sa.max_blocks_per_seq = dims.max_blocks_per_seq;
+    sa.partition_size = psize;
+    sa.max_partitions = nparts;
+    sa.causal = causal ? 1 : 0;
+    if (gqa::launch_schedule(sa, s) != hipSuccess) return GQA_ERR_LAUNCH;
+
+    gqa::MixedArgs ma;
+    ma.prefill = p;
+    gqa::DecodeArgs& d = ma.decode;
+    d.out = out;
+    d.query = query;
+    d.key_cache = key_cache;
+    d.value_cache = value_cache;
+    d.block_tables = block_tables;
+    d.seq_lens = seq_lens;
+    d.query_start_loc = query_start_loc;
+    d.partial_out = nparts > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+    d.partial_lse = nparts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * dims.head_dim * sizeof(float))) : nullptr;
+    d.num_heads = dims.num_heads;
+    d.num_kv_heads = dims.num_kv_heads;
+    d.group = G;
+    d.num_blocks = dims.num_blocks;
+    d.max_blocks_per_seq = dims.max_blocks_per_seq;
+    d.num_tokens = num_tokens;
+    d.partition_size = psize;
+    d.max_partitions = nparts;
+    d.scale_log2 = scale_log2;
+    ma.units = units;
+    ma.unit_count = count;
+    hipError_t e = gqa::launch_mixed(ma, dims.head_dim, out_f32, (int)(cap * dims.num_kv_heads), s);
+    if (e != hipSuccess || nparts <= 1) return status_from(e);
+    gqa::ReduceArgs r;
+    r.out = out;
+    r.partial_out = d.partial_out;
+    r.partial_lse = d.partial_lse;
+    r.seq_lens = seq_lens;
+    r.query_start_loc = query_start_loc;
+    r.num_heads = dims.num_heads;
+    r.num_kv_heads = dims.num_kv_heads;
+    r.group = G;
+    r.max_blocks_per_seq = dims.max_blocks_per_seq;
+    r.max_partitions = nparts;
+    r.partition_size = psize;
+    r.num_tokens = num_tokens;
+    r.skip_single = 1;
+    return status_from(gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, s));
+  }
+
+  // fp32: prefill kernel, then the decode of paged_gqa_decode
+  {
+    int ps = 0, np = 0;
+    if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
+    if (use_stream(dims, partition_size)) {
+      if (workspace == nullptr || workspace_bytes < stream_bytes(dims, gqa::kStreamWorkersPerGroup))
+        return GQA_ERR_WORKSPACE;
+    } else {
+      const size_t need = partial_bytes(dims, np);
+      if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+    }
+  }
+  if (max_query_len > 1) {
+    const long long rpg = gqa::prefill_rows_per_group();
+    // Upper bound on row tiles: every prefill sequence wastes at most one partial tile.
+    const long long prefill_seqs = std::min<long long>(dims.num_seqs, num_tokens / 2);
+    const long long tiles = ((long long)num_tokens * G + rpg - 1) / rpg + prefill_seqs;
+    const long long groups = tiles * dims.num_kv_heads;
+    if (groups > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    hipError_t e = gqa::launch_prefill(p, dims.head_dim, true, out_f32, (int)groups, s);
+    if (e != hipSuccess) return GQA_ERR_LAUNCH;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
+                    max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
 }
 
 }  // namespace
@@ -315,136 +462,25 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
                                      const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
                                      int32_t max_seq_len, gqa_dims dims, float scale, int32_t partition_size,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_dims(dims);
-  if (st != GQA_OK) return st;
-  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || num_tokens < 0 || max_query_len < 0) return GQA_ERR_INVALID_ARG;
-  if (max_query_len > max_seq_len) return GQA_ERR_INVALID_ARG;
-  if (dims.num_seqs == 0 || num_tokens == 0) {
-    int ps = 0, np = 0;
-    return partitioning(max_seq_len, partition_size, &ps, &np) ? GQA_OK : GQA_ERR_INVALID_ARG;
-  }
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc)
-    return GQA_ERR_INVALID_ARG;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
-  const int G = dims.num_heads / dims.num_kv_heads;
-  const float scale_log2 = scale * 1.4426950408889634f;
+  return run_mixed(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
+                   max_query_len, max_seq_len, dims, scale, partition_size, workspace, workspace_bytes,
+                   reinterpret_cast<hipStream_t>(stream), true);
+}
 
-  gqa::PrefillArgs p;
-  p.out = out;
-  p.query = query;
-  p.key_cache = key_cache;
-  p.value_cache = value_cache;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  p.query_start_loc = query_start_loc;
-  p.num_seqs = dims.num_seqs;
-  p.num_heads = dims.num_heads;
-  p.num_kv_heads = dims.num_kv_heads;
-  p.group = G;
-  p.num_blocks = dims.num_blocks;
-  p.max_blocks_per_seq = dims.max_blocks_per_seq;
-  p.num_tokens = num_tokens;
-  p.scale_log2 = scale_log2;
+size_t paged_cross_attention_workspace_size(gqa_dims dims, int32_t num_tokens, int32_t max_encoder_len,
+                                            int32_t partition_size) {
+  if (check_dims(dims) != GQA_OK) return 0;
+  return mixed_bytes(dims, num_tokens, max_encoder_len, partition_size);
+}
 
-  if (!kv_f32) {
-    // scheduling pass + fused prefill/decode kernel (+ merge of split decodes)
-    int psize = 0, nparts = 0;
-    if (!mixed_decode_split(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
-    const long long cap = mixed_unit_capacity(dims, num_tokens, nparts);
-    if (cap >= kMaxMixedUnits || cap * dims.num_kv_heads > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-    const size_t need = mixed_bytes(dims, num_tokens, max_seq_len, partition_size);
-    if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
-    char* ws = reinterpret_cast<char*>(workspace);
-    gqa::MixedUnit* units = reinterpret_cast<gqa::MixedUnit*>(ws);
-    ws += align_up((size_t)cap * sizeof(gqa::MixedUnit));
-    int* count = reinterpret_cast<int*>(ws);
-    ws += align_up(sizeof(int));
-    const size_t rows = (size_t)dims.num_seqs * dims.num_heads * nparts;
-
-    gqa::ScheduleArgs sa;
-    sa.seq_lens = seq_lens;
-    sa.query_start_loc = query_start_loc;
-    sa.units = units;
-    sa.unit_count = count;
-    sa.unit_capacity = (int)cap;
-    sa.num_seqs = dims.num_seqs;
-    sa.num_tokens = num_tokens;
-    sa.max_query_len = max_query_len;
-    sa.group = G;
-    sa.rows_per_group = gqa::prefill_lds_rows_per_group();
-    sa.max_blocks_per_seq = dims.max_blocks_per_seq;
-    sa.partition_size = psize;
-    sa.max_partitions = nparts;
-    if (gqa::launch_schedule(sa, s) != hipSuccess) return GQA_ERR_LAUNCH;
-
-    gqa::MixedArgs ma;
-    ma.prefill = p;
-    gqa::DecodeArgs& d = ma.decode;
-    d.out = out;
-    d.query = query;
-    d.key_cache = key_cache;
-    d.value_cache = value_cache;
-    d.block_tables = block_tables;
-    d.seq_lens = seq_lens;
-    d.query_start_loc = query_start_loc;
-    d.partial_out = nparts > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-    d.partial_lse = nparts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * dims.head_dim * sizeof(float))) : nullptr;
-    d.num_heads = dims.num_heads;
-    d.num_kv_heads = dims.num_kv_heads;
-    d.group = G;
-    d.num_blocks = dims.num_blocks;
-    d.max_blocks_per_seq = dims.max_blocks_per_seq;
-    d.num_tokens = num_tokens;
-    d.partition_size = psize;
-    d.max_partitions = nparts;
-    d.scale_log2 = scale_log2;
-    ma.units = units;
-    ma.unit_count = count;
-    hipError_t e = gqa::launch_mixed(ma, dims.head_dim, out_f32, (int)(cap * dims.num_kv_heads), s);
-    if (e != hipSuccess || nparts <= 1) return status_from(e);
-    gqa::ReduceArgs r;
-    r.out = out;
-    r.partial_out = d.partial_out;
-    r.partial_lse = d.partial_lse;
-    r.seq_lens = seq_lens;
-    r.query_start_loc = query_start_loc;
-    r.num_heads = dims.num_heads;
-    r.num_kv_heads = dims.num_kv_heads;
-    r.group = G;
-    r.max_blocks_per_seq = dims.max_blocks_per_seq;
-    r.max_partitions = nparts;
-    r.partition_size = psize;
-    r.num_tokens = num_tokens;
-    r.skip_single = 1;
-    return status_from(gqa::launch_reduce(r, dims.head_dim, out_f32, dims.num_seqs, s));
-  }
-
-  // fp32: prefill kernel, then the decode of paged_gqa_decode
-  {
-    int ps = 0, np = 0;
-    if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
-    if (use_stream(dims, partition_size)) {
-      if (workspace == nullptr || workspace_bytes < stream_bytes(dims, gqa::kStreamWorkersPerGroup))
-        return GQA_ERR_WORKSPACE;
-    } else {
-      const size_t need = partial_bytes(dims, np);
-      if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
-    }
-  }
-  if (max_query_len > 1) {
-    const long long rpg = gqa::prefill_rows_per_group();
-    // Upper bound on row tiles: every prefill sequence wastes at most one partial tile.
-    const long long prefill_seqs = std::min<long long>(dims.num_seqs, num_tokens / 2);
-    const long long tiles = ((long long)num_tokens * G + rpg - 1) / rpg + prefill_seqs;
-    const long long groups = tiles * dims.num_kv_heads;
-    if (groups > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-    hipError_t e = gqa::launch_prefill(p, dims.head_dim, true, out_f32, (int)groups, s);
-    if (e != hipSuccess) return GQA_ERR_LAUNCH;
-  }
-  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
-                    max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
+int32_t paged_cross_attention(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, const int32_t* encoder_lens,
+                              const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                              int32_t max_encoder_len, gqa_dims dims, float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return run_mixed(out, query, key_cache, value_cache, block_tables, encoder_lens, query_start_loc, num_tokens,
+                   max_query_len, max_encoder_len, dims, scale, partition_size, workspace, workspace_bytes,
+                   reinterpret_cast<hipStream_t>(stream), false);
 }
 
 }  // extern "C"

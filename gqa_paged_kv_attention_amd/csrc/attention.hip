@@ -232,7 +232,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   int L = a.seq_lens[b];
   L = max(0, min(L, a.max_blocks_per_seq * kPage));
   const int prior = L - q_len;
-  if (prior < 0) return;
+  if (a.causal && prior < 0) return;
+  // last key visible to new token j (causal), or every key (cross-attention)
+  auto last_key = [&](int j) { return a.causal ? prior + j : L - 1; };
   const int rows_total = q_len * G;
   const int n_row_tiles = (rows_total + RWG - 1) / RWG;
   // heaviest row tile (most keys) of the sequence first
@@ -251,16 +253,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int r = r0 + nt * 16 + n;
     const bool valid = r < rows_total;
     const int j = r / G, g = r % G;
-    lim[nt] = valid ? prior + j : -1;
+    lim[nt] = valid ? last_key(j) : -1;
     tok[nt] = valid ? q0 + j : -1;
     head[nt] = kv * G + g;
     const elem_t* qrow = valid ? reinterpret_cast<const elem_t*>(a.query) + ((size_t)tok[nt] * a.num_heads + head[nt]) * D
                                : nullptr;
     Tile::load_q(qf[nt], qrow, lane);
   }
-  const int lim_lo = prior + r0 / G;                                   // first row of the wave
-  const int lim_hi = prior + min(q_len - 1, (r0 + NTW * 16 - 1) / G);  // last row of the wave
-  const int n_tiles = (lim_hi + 1 + kTile - 1) / kTile;
+  const int lim_lo = last_key(r0 / G);                                   // first row of the wave
+  const int lim_hi = last_key(min(q_len - 1, (r0 + NTW * 16 - 1) / G));  // last row of the wave
+  const int n_tiles = (lim_hi + 1 + kTile - 1) / kTile;                  // 0 when no key is visible
   const int npages = (L + kPage - 1) / kPage;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
 

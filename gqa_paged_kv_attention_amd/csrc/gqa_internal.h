@@ -71,6 +71,7 @@ struct PrefillArgs {
   int max_blocks_per_seq;
   int num_tokens;
   float scale_log2;
+  int causal;                       // 1: bottom-right causal; 0: every row sees all seq_len keys
 };
 
 struct ReduceArgs {
@@ -140,6 +141,7 @@ struct ScheduleArgs {
   int max_blocks_per_seq;
   int partition_size;               // decode partitions (tokens, multiple of 32)
   int max_partitions;
+  int causal;                       // as PrefillArgs::causal
 };
 struct MixedArgs {
   PrefillArgs prefill;

@@ -147,8 +147,9 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 
 // Row tile rt (rows [rt * R, rt * R + R) of the r = j * G + g order, R =
 // kRowsPerGroup) of sequence b (new tokens [q0, q1), seq_lens[b] = seq_len)
-// against kv head kv.  sK / sV: two LDS buffers
-// of KBUF and VBUF elements each.
+// against kv head kv.  Causal: token j sees keys up to seq_len - q_len + j;
+// otherwise (cross-attention) every row sees all seq_len keys, and q_len may
+// exceed seq_len.  sK / sV: two LDS buffers of KBUF and VBUF elements each.
 template <int D, int NTW, class OutT>
 __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int q0, int q1, int seq_len, int kv,
                                              uint16_t* sK, uint16_t* sV) {
@@ -158,8 +159,10 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   if (q1 > a.num_tokens || q0 < 0) return;
   const int L = max(0, min(seq_len, a.max_blocks_per_seq * kPage));
   const int prior = L - q_len;
-  if (prior < 0) return;
+  if (a.causal && prior < 0) return;
   const int rows_total = q_len * G;
+  // last key visible to new token j
+  auto last_key = [&](int j) { return a.causal ? prior + j : L - 1; };
 
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, q = lane >> 4;
@@ -181,7 +184,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
     const int r = r0 + nt * 16 + n;
     const bool valid = r < rows_total;
     const int j = r / G, g = r % G;
-    lim[nt] = valid ? prior + j : -1;
+    lim[nt] = valid ? last_key(j) : -1;
     tok[nt] = valid ? q0 + j : -1;
     head[nt] = kv * G + g;
     const uint16_t* qrow =
@@ -196,10 +199,11 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
       qf[nt][c] = x;
     }
   }
-  const int lim_lo = prior + r0 / G;
-  const int lim_hi = wave_rows ? prior + min(q_len - 1, (r0 + S::kRowsPerWave - 1) / G) : -1;
-  const int group_hi = prior + min(q_len - 1, (rt * S::kRowsPerGroup + S::kRowsPerGroup - 1) / G);
-  const int n_tiles = group_hi / kKeyTile + 1;
+  const int lim_lo = last_key(r0 / G);
+  const int lim_hi = wave_rows ? last_key(min(q_len - 1, (r0 + S::kRowsPerWave - 1) / G)) : -1;
+  const int group_hi = last_key(min(q_len - 1, (rt * S::kRowsPerGroup + S::kRowsPerGroup - 1) / G));
+  // no tile when no key is visible (an empty encoder sequence): zero rows
+  const int n_tiles = group_hi < 0 ? 0 : group_hi / kKeyTile + 1;
   const int npages = (L + kPage - 1) / kPage;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
   const char* kc = reinterpret_cast<const char*>(a.key_cache) + (size_t)kv * (kPage * D * 2);
@@ -244,13 +248,15 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   // iteration t, so each load has a whole iteration to arrive.
   uint4 kreg[S::CH], vreg[S::CH];
   int raw[kTilePages];
-  fetch_pages(0, raw);
-  issue(raw, kreg, vreg);
-  fetch_pages(1, raw);
-  store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kKeyTile > L);
-  if (n_tiles > 1) issue(raw, kreg, vreg);
-  fetch_pages(2, raw);
-  __syncthreads();
+  if (n_tiles > 0) {                     // uniform over the work-group
+    fetch_pages(0, raw);
+    issue(raw, kreg, vreg);
+    fetch_pages(1, raw);
+    store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kKeyTile > L);
+    if (n_tiles > 1) issue(raw, kreg, vreg);
+    fetch_pages(2, raw);
+    __syncthreads();
+  }
 
   // LDS offsets of this lane's key rows (32-key half 0, products s = 0, 1;
   // token fed to row m as in TileBF16; half 1 is 32 rows further) and value
@@ -431,9 +437,10 @@ __device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* u
     return true;
   }
   const int prior = L - q_len;
-  if (prior < 0) return false;
+  if (a.causal && prior < 0) return false;
   *units = (q_len * a.group + a.rows_per_group - 1) / a.rows_per_group;
-  *cost = (prior + q_len - 1) / kTile + 1;
+  // tiles up to the last row's last visible key (all L keys without the mask)
+  *cost = (a.causal ? prior + q_len - 1 : max(L - 1, 0)) / kTile + 1;
   return false;
 }
 

@@ -65,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.chunked_prefill_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, Dims, f32, i32, vp, sz,
                                                  vp]
     lib.chunked_prefill_paged_decode.restype = i32
+    lib.paged_cross_attention_workspace_size.argtypes = [Dims, i32, i32, i32]
+    lib.paged_cross_attention_workspace_size.restype = sz
+    lib.paged_cross_attention.argtypes = list(lib.chunked_prefill_paged_decode.argtypes)
+    lib.paged_cross_attention.restype = i32
     _lib = lib
     return lib
 
@@ -230,6 +234,34 @@ def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, se
                                            _ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc), T,
                                            int(max_query_len), int(max_seq_len), dims, float(scale),
                                            int(partition_size), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def cross_workspace_size(dims: Dims, num_tokens: int, max_encoder_len: int, partition_size: int) -> int:
+    return int(load_library().paged_cross_attention_workspace_size(dims, int(num_tokens), int(max_encoder_len),
+                                                                    int(partition_size)))
+
+
+def paged_cross_attention(query, key_cache, value_cache, block_tables, encoder_lens, query_start_loc,
+                          max_query_len: int, max_encoder_len: int, scale: float, partition_size: int = 0,
+                          out=None, out_dtype=None, workspace=None, stream=None):
+    """Cross-attention of decoder rows ``query [T, Hq, d]`` over a static encoder cache -> ``out [T, Hq, d]``."""
+    lib = load_library()
+    _check_device(query, key_cache, value_cache, block_tables, encoder_lens, query_start_loc, out, workspace)
+    _check_int32(block_tables, encoder_lens, query_start_loc)
+    T, Hq, d = query.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(T, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=encoder_lens.shape[0], num_heads=Hq, key_cache=key_cache, block_tables=block_tables,
+                     q_dtype=query.dtype, out_dtype=out_dtype)
+    nbytes = int(lib.paged_cross_attention_workspace_size(dims, T, int(max_encoder_len), int(partition_size)))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
+    _call("paged_cross_attention",
+          lib.paged_cross_attention(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                    _ptr(encoder_lens), _ptr(query_start_loc), T, int(max_query_len),
+                                    int(max_encoder_len), dims, float(scale), int(partition_size), _ptr(ws), wsb,
+                                    _stream(stream)))
     return out
 
 

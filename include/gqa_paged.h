@@ -191,7 +191,8 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
  * P.V on fp16 matrix cores (P rounded to fp16, V converted from bf16):
  * precondition |V| < 65504, else results saturate.
  * fp32: a prefill kernel, then the decode of paged_gqa_decode (same meaning of
- * partition_size).  bf16 batches with 2^20 or more work units (num_tokens * G /
+ * partition_size).  Either dtype: a batch whose max_query_len is 1 (decodes
+ * only) runs the decode of paged_gqa_decode alone.  bf16 batches with 2^20 or more work units (num_tokens * G /
  * 128 + num_seqs * (1 + decode partitions)) return GQA_ERR_UNSUPPORTED.
  *
  * Workspace (device, >= chunked_prefill_paged_decode_workspace_size bytes for
@@ -206,6 +207,30 @@ int32_t chunked_prefill_paged_decode(void* out, const void* query, const void* k
                                      int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                                      gqa_dims dims, float scale, int32_t partition_size,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_cross_attention: attention of decoder rows over a static encoder
+ * cache ("[Core] More-efficient cross-attention parallel QKV computation",
+ * opening post: the queries come from the decoder, the keys and values from
+ * the encoder output, and after the prefill only queries are new, so the
+ * encoder cache is written once and never appended to).  Same arguments,
+ * layouts, workspace and precision as chunked_prefill_paged_decode, with
+ * encoder_lens in place of seq_lens and no causal mask: every query row of
+ * sequence b sees all encoder_lens[b] positions.  A sequence may have more
+ * query rows than encoder positions (max_query_len may exceed
+ * max_encoder_len); an empty encoder sequence gives zero rows.  A batch
+ * whose max_query_len is 1 runs the decode of paged_gqa_decode.
+ *
+ * Workspace: >= paged_cross_attention_workspace_size bytes for the same dims,
+ * num_tokens, max_encoder_len and partition_size.
+ */
+size_t paged_cross_attention_workspace_size(gqa_dims dims, int32_t num_tokens, int32_t max_encoder_len,
+                                            int32_t partition_size);
+int32_t paged_cross_attention(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, const int32_t* encoder_lens,
+                              const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                              int32_t max_encoder_len, gqa_dims dims, float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

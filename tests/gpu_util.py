@@ -48,6 +48,13 @@ class DeviceBatch:
                                                 out_dtype=out_dtype)
 
 
+    def cross(self, partition_size=0, out_dtype=torch.float32):
+        return ops.paged_cross_attention(self.query, self.key_cache, self.value_cache, self.block_tables,
+                                         self.seq_lens, self.query_start_loc, self.bt.max_query_len,
+                                         self.bt.max_seq_len, self.bt.scale, partition_size=partition_size,
+                                         out_dtype=out_dtype)
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     return t.float().cpu().numpy().astype(np.float64)

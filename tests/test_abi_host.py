@@ -29,6 +29,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = ops.declared_functions()
     assert {"reshape_and_cache", "paged_gqa_decode", "splitk_lse_reduce", "chunked_prefill_paged_decode",
             "paged_gqa_decode_workspace_size", "chunked_prefill_paged_decode_workspace_size",
+            "paged_cross_attention", "paged_cross_attention_workspace_size",
             "gqa_status_string", "gqa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -106,18 +107,42 @@ def test_mixed_and_reduce_validation(lib):
 
 
 def test_mixed_bf16_workspace(lib):
-    """bf16 mixed batches need the scheduled unit list (8 bytes per unit, at
+    """bf16 mixed batches need the scheduled unit list (32 bytes per unit, at
     least num_tokens * G / 128 prefill row tiles plus one unit per decode), a
-    count, and partials only when decodes are split."""
+    count, and partials only when decodes are split; a batch of decodes only
+    runs the decode, so the decode's workspace fits as well."""
     d = dims()                                     # 4 seqs, G = 4, bf16
     n = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 256, 0)
-    assert n % 256 == 0 and n >= (1000 * 4 // 128 + 4) * 8 + 4
-    # bigger batches need more list; a split adds the partials
-    assert lib.chunked_prefill_paged_decode_workspace_size(d, 4000, 256, 0) > n
+    assert n % 256 == 0 and n >= (1000 * 4 // 128 + 4) * 32 + 4
+    assert n >= lib.paged_gqa_decode_workspace_size(d, 256, 0)
+    # a split adds the partials of 16 partitions per (sequence, query head)
     split = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 8192, 512)
-    assert split >= n + 4 * 32 * 16 * 128 * 4
+    assert split >= (1000 * 4 // 128 + 4 * 17) * 32 + 4 * 32 * 16 * 128 * 4
+    assert split >= lib.paged_gqa_decode_workspace_size(d, 8192, 512)
     call = lambda ws, wsb: lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 100, 256,
                                                             d, 0.1, 0, ws, wsb, None)
     assert call(None, 0) == WORKSPACE
     assert call(FAKE, n - 1) == WORKSPACE
     assert lib.chunked_prefill_paged_decode_workspace_size(d, -1, 256, 0) == 0
+
+
+def cross(lib, d, num_tokens=10, max_query_len=20, max_encoder_len=10, ws=None, wsb=0, ptr=FAKE, qsl=FAKE):
+    return lib.paged_cross_attention(ptr, ptr, ptr, ptr, ptr, ptr, qsl, num_tokens, max_query_len, max_encoder_len,
+                                     d, 0.1, 0, ws, wsb, None)
+
+
+def test_cross_attention_validation(lib):
+    d = dims()
+    # a chunk may be longer than the encoder sequence: past validation, the
+    # missing workspace is reported (the causal call rejects the same lengths)
+    assert cross(lib, d) == WORKSPACE
+    assert lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 20, 10, d, 0.1, 0,
+                                            None, 0, None) == INVALID
+    assert cross(lib, d, qsl=None) == INVALID
+    assert cross(lib, d, ptr=None) == INVALID
+    assert cross(lib, d, max_query_len=-1) == INVALID
+    assert cross(lib, dims(head_dim=96)) == UNSUPPORTED
+    assert cross(lib, dims(num_seqs=0), ptr=None, qsl=None) == OK
+    n = lib.paged_cross_attention_workspace_size(d, 1000, 6400, 0)
+    assert n == lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 6400, 0)
+    assert cross(lib, d, num_tokens=1000, max_query_len=100, max_encoder_len=6400, ws=FAKE, wsb=n - 1) == WORKSPACE
