@@ -39,7 +39,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "e00a7813afbd4c5e94d1c6ca0e425841763649f63881043d5001778fa9c2a57c", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 649567028, "write_bytes_per_call": 6337586, "hbm_bytes_per_call": 655904614, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "0a2b4915b5648e17ee243a2143e0061c32c18f1276b9384bf91d0963a9078b53", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648796378, "write_bytes_per_call": 6338613, "hbm_bytes_per_call": 655134992, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-gqa-comparison", action="store_true")
     ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention leg")
+    ap.add_argument("--no-page-sizes", action="store_true", help="skip the 16/32/64-token page comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -202,6 +203,34 @@ def cross_attention_leg(dev, stream, reps):
     return res
 
 
+def page_size_leg(dev, stream, reps, seed):
+    """The decode call on the same workload (same lengths and seed) with 16-,
+    32- and 64-token pages: the kernels' tiles do not depend on the page size,
+    but larger pages make each (page, kv head) slab a longer contiguous read."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    res = {"workload": "llama31_8b_decode (64 seqs, Hq=32, Hkv=8, d=128, context U{512..4096}, bf16)",
+           "call": "paged_gqa_decode, partition_size 0"}
+    for bs in (16, 32, 64):
+        bt = wl.llama31_8b_decode(seed=seed, block_size=bs)
+        up = lambda a: ops.to_device(a, dev)
+        q, kc, vc, tb, sl = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.block_tables), up(bt.seq_lens)
+        out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tb,
+                             q_dtype=q.dtype, out_dtype=out.dtype)
+        ws = torch.zeros(max(ops.decode_workspace_size(dims, bt.max_seq_len, 0), 1), dtype=torch.uint8, device=dev)
+        f = lambda: ops.paged_gqa_decode(q, kc, vc, tb, sl, bt.max_seq_len, bt.scale, out=out, workspace=ws)
+        for _ in range(3):
+            f()
+        ms = event_time_ms(f, reps, stream)
+        res[f"bs{bs}"] = {"us": round(ms * 1e3, 2), "kv_gbs": round(bt.kv_bytes() / (ms * 1e-3) / 1e9, 1),
+                          "page_slab_bytes": bs * bt.head_dim * 2}
+        del q, kc, vc, out, ws
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -312,6 +341,9 @@ def main():
 
     if not args.no_cross:
         record["cross_attention"] = cross_attention_leg(dev, stream, 30)
+
+    if not args.no_page_sizes:
+        record["page_sizes"] = page_size_leg(dev, stream, 50, args.seed)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)

@@ -24,7 +24,7 @@ int check_dims(const gqa_dims& d) {
   if (d.kv_dtype != GQA_F32 && d.kv_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
   if (d.out_dtype != GQA_F32 && d.out_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
   if (d.head_dim != 64 && d.head_dim != 128) return GQA_ERR_UNSUPPORTED;
-  if (d.block_size != 16) return GQA_ERR_UNSUPPORTED;
+  if (d.block_size != 16 && d.block_size != 32 && d.block_size != 64) return GQA_ERR_UNSUPPORTED;
   if (d.q_dtype != d.kv_dtype) return GQA_ERR_UNSUPPORTED;
   if ((long long)d.max_blocks_per_seq * d.block_size > kMaxSeqLen) return GQA_ERR_UNSUPPORTED;
   if (d.num_seqs > 65535) return GQA_ERR_UNSUPPORTED;
@@ -84,7 +84,7 @@ size_t stream_bytes(const gqa_dims& d, int workers) {
 }
 
 int device_workers(const gqa_dims& d) {
-  return gqa::stream_workers(d.head_dim, d.kv_dtype == GQA_F32, d.out_dtype == GQA_F32,
+  return gqa::stream_workers(d.head_dim, d.block_size, d.kv_dtype == GQA_F32, d.out_dtype == GQA_F32,
                              d.num_heads / d.num_kv_heads, d.num_seqs);
 }
 
@@ -170,7 +170,7 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     a.num_tokens = num_tokens;
     a.num_workers = workers;
     a.scale_log2 = scale_log2;
-    hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, kv_f32, out_f32, stream);
+    hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, stream);
     if (e != hipSuccess) return GQA_ERR_LAUNCH;
     return status_from(gqa::launch_stream_reduce(a, dims.head_dim, out_f32, stream));
   }
@@ -199,7 +199,7 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   a.partition_size = psize;
   a.max_partitions = nparts;
   a.scale_log2 = scale_log2;
-  hipError_t e = gqa::launch_decode(a, dims.head_dim, kv_f32, out_f32, dims.num_seqs, stream);
+  hipError_t e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, stream);
   if (e != hipSuccess || nparts <= 1) return status_from(e);
   gqa::ReduceArgs r;
   r.out = out;
@@ -211,6 +211,7 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   r.num_kv_heads = dims.num_kv_heads;
   r.group = a.group;
   r.max_blocks_per_seq = dims.max_blocks_per_seq;
+  r.block_size = dims.block_size;
   r.max_partitions = nparts;
   r.partition_size = psize;
   r.num_tokens = num_tokens;
@@ -288,6 +289,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     sa.group = G;
     sa.rows_per_group = gqa::prefill_lds_rows_per_group();
     sa.max_blocks_per_seq = dims.max_blocks_per_seq;
+    sa.block_size = dims.block_size;
     sa.partition_size = psize;
     sa.max_partitions = nparts;
     sa.causal = causal ? 1 : 0;
@@ -316,7 +318,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     d.scale_log2 = scale_log2;
     ma.units = units;
     ma.unit_count = count;
-    hipError_t e = gqa::launch_mixed(ma, dims.head_dim, out_f32, (int)(cap * dims.num_kv_heads), s);
+    hipError_t e = gqa::launch_mixed(ma, dims.head_dim, dims.block_size, out_f32, (int)(cap * dims.num_kv_heads), s);
     if (e != hipSuccess || nparts <= 1) return status_from(e);
     gqa::ReduceArgs r;
     r.out = out;
@@ -328,6 +330,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     r.num_kv_heads = dims.num_kv_heads;
     r.group = G;
     r.max_blocks_per_seq = dims.max_blocks_per_seq;
+    r.block_size = dims.block_size;
     r.max_partitions = nparts;
     r.partition_size = psize;
     r.num_tokens = num_tokens;
@@ -354,7 +357,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     const long long tiles = ((long long)num_tokens * G + rpg - 1) / rpg + prefill_seqs;
     const long long groups = tiles * dims.num_kv_heads;
     if (groups > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-    hipError_t e = gqa::launch_prefill(p, dims.head_dim, true, out_f32, (int)groups, s);
+    hipError_t e = gqa::launch_prefill(p, dims.head_dim, dims.block_size, true, out_f32, (int)groups, s);
     if (e != hipSuccess) return GQA_ERR_LAUNCH;
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, num_tokens,
@@ -400,7 +403,7 @@ int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, v
   a.num_kv_heads = dims.num_kv_heads;
   a.num_blocks = dims.num_blocks;
   a.max_blocks_per_seq = dims.max_blocks_per_seq;
-  return status_from(gqa::launch_cache_write(a, dims.head_dim, dims.kv_dtype == GQA_F32,
+  return status_from(gqa::launch_cache_write(a, dims.head_dim, dims.block_size, dims.kv_dtype == GQA_F32,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -443,6 +446,7 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
   r.num_kv_heads = dims.num_kv_heads;
   r.group = dims.num_heads / dims.num_kv_heads;
   r.max_blocks_per_seq = dims.max_blocks_per_seq;
+  r.block_size = dims.block_size;
   r.max_partitions = max_partitions;
   r.partition_size = partition_size;
   r.num_tokens = query_start_loc ? 0x7fffffff : dims.num_seqs;

@@ -60,7 +60,7 @@ void stream_decode_kernel(StreamArgs a) {
     if (b < B) {
       int row;
       const bool dec = stream_is_decode(a, b, &row);
-      const int L = dec ? clamp_len(a.seq_lens[b], a.max_blocks_per_seq) : 0;
+      const int L = dec ? clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS) : 0;
       v = (L + kTile - 1) / kTile * a.num_kv_heads;
       if (dec && L == 0 && (b % gridDim.x) == (int)blockIdx.x) {
         // an empty decode sequence has a zero output row
@@ -122,7 +122,7 @@ void stream_decode_kernel(StreamArgs a) {
     const int tile_end = (int)min((long long)nt, hi - unit0);
     int row;
     stream_is_decode(a, b, &row);
-    const int L = clamp_len(a.seq_lens[b], a.max_blocks_per_seq);
+    const int L = clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS);
 
     typename Tile::Q qf[NT];
     load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
@@ -229,8 +229,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0) return;
-  int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_blocks_per_seq * kPage));
+  const int L = clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS);
   const int prior = L - q_len;
   if (a.causal && prior < 0) return;
   // last key visible to new token j (causal), or every key (cross-attention)
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int lim_lo = last_key(r0 / G);                                   // first row of the wave
   const int lim_hi = last_key(min(q_len - 1, (r0 + NTW * 16 - 1) / G));  // last row of the wave
   const int n_tiles = (lim_hi + 1 + kTile - 1) / kTile;                  // 0 when no key is visible
-  const int npages = (L + kPage - 1) / kPage;
+  const int npages = (L + Tile::kBS - 1) / Tile::kBS;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
 
   float m[NTW], l[NTW];
@@ -278,15 +277,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   for (int it = 0; it < n_tiles; ++it) {
     const int tb = it * kTile;
-    const int pg = tb / kPage;
-    const int pA = page_at(bt, pg, a.num_blocks);
-    const int pB = page_at(bt, min(pg + 1, npages - 1), a.num_blocks);
+    TilePages<Tile, D> pg;
+    pg.fetch(bt, it, npages, a.num_blocks);
     typename Tile::K kf;
     typename Tile::V vf;
-    Tile::load_k(kf, page_ptr<elem_t>(a.key_cache, pA, a.num_kv_heads, kv, D),
-                 page_ptr<elem_t>(a.key_cache, pB, a.num_kv_heads, kv, D), lane);
-    Tile::load_v(vf, page_ptr<elem_t>(a.value_cache, pA, a.num_kv_heads, kv, D),
-                 page_ptr<elem_t>(a.value_cache, pB, a.num_kv_heads, kv, D), lane);
+    load_tile<Tile, D>(kf, vf, pg, a.key_cache, a.value_cache, a.num_kv_heads, kv, lane);
     const bool masked = tb + kTile - 1 > lim_lo;
     if (tb + kTile > L) Tile::mask_v(vf, tb, L, lane);
 #pragma unroll
@@ -320,76 +315,70 @@ hipError_t decode_dispatch_nt(const DecodeArgs& a, int num_seqs, hipStream_t str
   return hipGetLastError();
 }
 
-template <class OutT>
-hipError_t decode_dispatch_out(const DecodeArgs& a, int D, bool kv_f32, int num_seqs, hipStream_t s) {
-  if (kv_f32) {
-    return D == 64 ? decode_dispatch_nt<TileF32<64>, 64, OutT>(a, num_seqs, s)
-                   : decode_dispatch_nt<TileF32<128>, 128, OutT>(a, num_seqs, s);
-  }
-  return D == 64 ? decode_dispatch_nt<TileBF16<64>, 64, OutT>(a, num_seqs, s)
-                 : decode_dispatch_nt<TileBF16<128>, 128, OutT>(a, num_seqs, s);
-}
-
-// Resolve the stream-decode instantiation for (D, dtype, out dtype, group) and
-// hand it to `f`.
+// Call f(Tile type tag, head dim tag) for the cache dtype, head_dim and page size.
 template <class F>
-auto with_stream_kernel(int D, bool kv_f32, bool out_f32, int group, F f) {
-  typedef void (*K)(StreamArgs);
-  K k;
-#define GQA_PICK(TILE, DD, NT)                                                                     \
-  k = out_f32 ? (K)stream_decode_kernel<TILE<DD>, DD, NT, float>                                  \
-              : (K)stream_decode_kernel<TILE<DD>, DD, NT, uint16_t>
-  if (kv_f32) {
-    if (D == 64) { if (group <= 16) GQA_PICK(TileF32, 64, 1); else GQA_PICK(TileF32, 64, 2); }
-    else { if (group <= 16) GQA_PICK(TileF32, 128, 1); else GQA_PICK(TileF32, 128, 2); }
-  } else {
-    if (D == 64) { if (group <= 16) GQA_PICK(TileBF16, 64, 1); else GQA_PICK(TileBF16, 64, 2); }
-    else { if (group <= 16) GQA_PICK(TileBF16, 128, 1); else GQA_PICK(TileBF16, 128, 2); }
-  }
-#undef GQA_PICK
-  return f(k);
+auto with_tile(int D, int block_size, bool kv_f32, F f) {
+  return with_block_size(block_size, [&](auto bs) {
+    constexpr int BS = decltype(bs)::value;
+    if (kv_f32)
+      return D == 64 ? f(TileF32<64, BS>{}, std::integral_constant<int, 64>{})
+                     : f(TileF32<128, BS>{}, std::integral_constant<int, 128>{});
+    return D == 64 ? f(TileBF16<64, BS>{}, std::integral_constant<int, 64>{})
+                   : f(TileBF16<128, BS>{}, std::integral_constant<int, 128>{});
+  });
 }
 
-template <class OutT>
-hipError_t prefill_dispatch_out(const PrefillArgs& a, int D, bool kv_f32, int groups, hipStream_t s) {
-  dim3 grid(groups), block(kThreads);
-  if (kv_f32) {
-    if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel<TileF32<64>, 64, kPrefillNTW, OutT>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<TileF32<128>, 128, kPrefillNTW, OutT>), grid, block, 0, s, a);
-  } else {
-    if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel<TileBF16<64>, 64, kPrefillNTW, OutT>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<TileBF16<128>, 128, kPrefillNTW, OutT>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+// Resolve the stream-decode instantiation for (D, page size, dtype, out dtype,
+// group) and hand it to `f`.
+template <class F>
+auto with_stream_kernel(int D, int block_size, bool kv_f32, bool out_f32, int group, F f) {
+  typedef void (*K)(StreamArgs);
+  K k = with_tile(D, block_size, kv_f32, [&](auto tile, auto dd) {
+    typedef decltype(tile) Tile;
+    constexpr int DD = decltype(dd)::value;
+    if (group <= 16)
+      return out_f32 ? (K)stream_decode_kernel<Tile, DD, 1, float> : (K)stream_decode_kernel<Tile, DD, 1, uint16_t>;
+    return out_f32 ? (K)stream_decode_kernel<Tile, DD, 2, float> : (K)stream_decode_kernel<Tile, DD, 2, uint16_t>;
+  });
+  return f(k);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool kv_f32, bool out_f32, int num_seqs,
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs,
                          hipStream_t stream) {
-  return out_f32 ? decode_dispatch_out<float>(a, head_dim, kv_f32, num_seqs, stream)
-                 : decode_dispatch_out<uint16_t>(a, head_dim, kv_f32, num_seqs, stream);
+  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+    typedef decltype(tile) Tile;
+    constexpr int DD = decltype(dd)::value;
+    return out_f32 ? decode_dispatch_nt<Tile, DD, float>(a, num_seqs, stream)
+                   : decode_dispatch_nt<Tile, DD, uint16_t>(a, num_seqs, stream);
+  });
 }
 
 int prefill_rows_per_group() { return PrefillShape<kPrefillNTW>::kRowsPerGroup; }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,
-                          hipStream_t stream) {
-  return out_f32 ? prefill_dispatch_out<float>(a, head_dim, kv_f32, grid_groups, stream)
-                 : prefill_dispatch_out<uint16_t>(a, head_dim, kv_f32, grid_groups, stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                          int grid_groups, hipStream_t stream) {
+  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+    typedef decltype(tile) Tile;
+    constexpr int DD = decltype(dd)::value;
+    if (out_f32)
+      hipLaunchKernelGGL((prefill_kernel<Tile, DD, kPrefillNTW, float>), dim3(grid_groups), dim3(kThreads), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<Tile, DD, kPrefillNTW, uint16_t>), dim3(grid_groups), dim3(kThreads), 0,
+                         stream, a);
+    return hipGetLastError();
+  });
 }
 
-int stream_workers(int head_dim, bool kv_f32, bool out_f32, int group, int num_seqs) {
+int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs) {
   int dev = 0, cus = 256, per_cu = 2;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     const size_t lds = (size_t)(num_seqs + 1) * sizeof(int);
-    with_stream_kernel(head_dim, kv_f32, out_f32, group, [&](void (*k)(StreamArgs)) {
+    with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [&](void (*k)(StreamArgs)) {
       int blocks = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(k), kThreads, lds) ==
               hipSuccess && blocks > 0)
@@ -401,10 +390,11 @@ int stream_workers(int head_dim, bool kv_f32, bool out_f32, int group, int num_s
   return cus * per_cu * kWaves;
 }
 
-hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream) {
+hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                                hipStream_t stream) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
   const dim3 grid(a.num_workers / kWaves), block(kThreads);
-  return with_stream_kernel(head_dim, kv_f32, out_f32, a.group, [&](void (*k)(StreamArgs)) {
+  return with_stream_kernel(head_dim, block_size, kv_f32, out_f32, a.group, [&](void (*k)(StreamArgs)) {
     hipLaunchKernelGGL(k, grid, block, lds, stream, a);
     return hipGetLastError();
   });

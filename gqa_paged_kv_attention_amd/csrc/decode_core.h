@@ -19,9 +19,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 
-template <class T>
+// Base of page `page`, kv head kv, in a cache of BS-token pages.
+template <class T, int BS>
 __device__ __forceinline__ const T* page_ptr(const void* cache, int page, int num_kv_heads, int kv, int D) {
-  return reinterpret_cast<const T*>(cache) + ((size_t)page * num_kv_heads + kv) * (size_t)(kPage * D);
+  return reinterpret_cast<const T*>(cache) + ((size_t)page * num_kv_heads + kv) * (size_t)(BS * D);
 }
 
 // One online-softmax + P.V step for a 16-row block.  `s` holds the block's 8
@@ -98,13 +99,23 @@ __device__ __forceinline__ void load_group_query(typename Tile::Q qf[NT], const 
 // is clamped to the last tile, whose re-read hits in cache), which keeps the
 // load count per iteration fixed and lets the compiler wait on just the
 // current tile's loads.
+// Pages of tile `it`: with 16-token pages the two halves are pages 2 it and
+// 2 it + 1 (the second clamped to the last page); with 32- or 64-token pages
+// both halves sit in page 32 it / BS, from token (32 it) mod BS on.
 template <class Tile, int D>
 struct TilePages {
+  static constexpr int BS = Tile::kBS;
   int pA, pB;
+  int off;                                  // in-page token of the tile's first key (BS > 16)
   __device__ __forceinline__ void fetch(const int32_t* bt, int it, int npages, int num_blocks) {
-    const int pg = it * (kTile / kPage);
-    pA = page_at(bt, pg, num_blocks);
-    pB = page_at(bt, min(pg + 1, npages - 1), num_blocks);
+    if constexpr (BS == kHalf) {
+      pA = page_at(bt, 2 * it, num_blocks);
+      pB = page_at(bt, min(2 * it + 1, npages - 1), num_blocks);
+      off = 0;
+    } else {
+      pA = pB = page_at(bt, it * kTile / BS, num_blocks);
+      off = it * kTile % BS;
+    }
   }
 };
 
@@ -112,10 +123,18 @@ template <class Tile, int D>
 __device__ __forceinline__ void load_tile(typename Tile::K& kf, typename Tile::V& vf, const TilePages<Tile, D>& pg,
                                           const void* kc, const void* vc, int num_kv_heads, int kv, int lane) {
   typedef typename Tile::elem_t elem_t;
-  Tile::load_k(kf, page_ptr<elem_t>(kc, pg.pA, num_kv_heads, kv, D), page_ptr<elem_t>(kc, pg.pB, num_kv_heads, kv, D),
-               lane);
-  Tile::load_v(vf, page_ptr<elem_t>(vc, pg.pA, num_kv_heads, kv, D), page_ptr<elem_t>(vc, pg.pB, num_kv_heads, kv, D),
-               lane);
+  constexpr int BS = Tile::kBS;
+  const elem_t* kA = page_ptr<elem_t, BS>(kc, pg.pA, num_kv_heads, kv, D);
+  const elem_t* vA = page_ptr<elem_t, BS>(vc, pg.pA, num_kv_heads, kv, D);
+  if constexpr (BS == kHalf) {
+    Tile::load_k(kf, kA, page_ptr<elem_t, BS>(kc, pg.pB, num_kv_heads, kv, D), lane);
+    Tile::load_v(vf, vA, page_ptr<elem_t, BS>(vc, pg.pB, num_kv_heads, kv, D), lane);
+  } else {
+    kA += pg.off * D;
+    vA += pg.off;
+    Tile::load_k(kf, kA, kA + kHalf * D, lane);
+    Tile::load_v(vf, vA, vA + kHalf, lane);
+  }
 }
 
 template <class Tile, int NT>
@@ -138,7 +157,7 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
                                           const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
                                           int L, int lim, int it0, int it1, int step, float scale_log2, int lane) {
   if (it0 >= it1) return;
-  const int npages = (L + kPage - 1) / kPage;
+  const int npages = (L + Tile::kBS - 1) / Tile::kBS;
   if constexpr (!Tile::kPipelined) {
     for (int it = it0; it < it1; it += step) {
       typename Tile::K kf;
@@ -172,8 +191,8 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
 }
 
 // Clamp a sequence length into what the block table can address.
-__device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq) {
-  return max(0, min(L, max_blocks_per_seq * kPage));
+__device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq, int block_size) {
+  return max(0, min(L, max_blocks_per_seq * block_size));
 }
 
 // ---------------------------------------------------------------------------
@@ -214,7 +233,7 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   typename Tile::Q qf[NT];
   load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
 
-  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq), a.max_partitions * a.partition_size);
+  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq, Tile::kBS), a.max_partitions * a.partition_size);
   const int nparts = (L + a.partition_size - 1) / a.partition_size;
   OutT* out = reinterpret_cast<OutT*>(a.out);
 

@@ -24,15 +24,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gqa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kTile = 32;        // key tokens per tile (two 16-token pages)
-constexpr int kPage = 16;        // block_size
+constexpr int kTile = 32;        // key tokens per tile (two 16-token halves)
+constexpr int kHalf = 16;        // tokens per half tile; pages hold 16, 32 or 64 tokens
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Host dispatch: call f(std::integral_constant<int, BS>) for a page size of
+// 16, 32 or 64 tokens (the only sizes the library is built for).
+template <class F>
+auto with_block_size(int block_size, F f) {
+  if (block_size == 64) return f(std::integral_constant<int, 64>{});
+  if (block_size == 32) return f(std::integral_constant<int, 32>{});
+  return f(std::integral_constant<int, 16>{});
+}
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -130,24 +141,30 @@ __device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_b
 }
 
 // ---------------------------------------------------------------------------
-// Tile operations, specialised by cache dtype.  A "tile" is 32 key tokens of
-// one kv head spread over two pages (A = tokens 0..15, B = tokens 16..31).
-// Each lane ends a Q.K^T product holding 8 scores per 16-row block, indexed
-// idx = 0..7; token_offset(q, idx) gives their key offsets inside the tile.
+// Tile operations, specialised by cache dtype and page size BS.  A "tile" is
+// 32 key tokens of one kv head in two 16-token halves (A = tokens 0..15, B =
+// tokens 16..31).  Each half lies inside one page: with 16-token pages the
+// halves are two pages, with 32- or 64-token pages they are consecutive runs
+// of one page, so the tile does not depend on the page size.  The loads take
+// the address of each half's first token: key rows are D elements apart in
+// any page, value channels BS elements apart.  Each lane ends a Q.K^T product
+// holding 8 scores per 16-row block, indexed idx = 0..7; token_offset(q, idx)
+// gives their key offsets inside the tile.
 // ---------------------------------------------------------------------------
 
 // bf16 caches: v_mfma_f32_16x16x32_bf16.
 //  - Q.K^T: two products per 16-row block, each over 16 tokens.  Product s
-//    feeds row m of A with token (m < 8 ? page A : page B), slot
+//    feeds row m of A with token (m < 8 ? half A : half B), offset
 //    (m & 3) + 8 * ((m >> 2) & 1) + 4 * s, and k slots 8q..8q+7 of chunk kk with
 //    channels 32 kk + 8q .. +7.  Lane group q then holds tokens 8q + idx.
 //  - P.V: one product per 16 channels over the whole 32-token tile; lane group
-//    q supplies k slots 8q..8q+7 = tokens 8q .. 8q+7 (page q >= 2 ? B : A,
-//    slots 8 (q & 1) ..), a contiguous 16-byte run of the channel-major page.
+//    q supplies k slots 8q..8q+7 = tokens 8q .. 8q+7 (half q >= 2 ? B : A,
+//    offsets 8 (q & 1) ..), a contiguous 16-byte run of the channel-major page.
 //  - P is fed as a hi/lo pair of bf16 (p = hi + lo to ~2^-16 relative), so the
 //    P.V product keeps fp32-grade weights.
-template <int D>
+template <int D, int BS>
 struct TileBF16 {
+  static constexpr int kBS = BS;
   static constexpr bool kPipelined = true;  // double-buffered tile loop
   static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
   static constexpr int DT = D / 16;   // 16-channel blocks of the output
@@ -159,7 +176,7 @@ struct TileBF16 {
   __device__ __forceinline__ static int token_offset(int q, int idx) { return 8 * q + idx; }
   __device__ __forceinline__ static int v_token_offset(int q, int e) { return 8 * q + e; }
 
-  // kA/kB: key page base for this kv head ([bs][D] elements).
+  // kA/kB: key row of the first token of half A / B (rows D elements apart).
   __device__ __forceinline__ static void load_k(K& k, const elem_t* kA, const elem_t* kB, int lane) {
     const int m = lane & 15, q = lane >> 4;
     const elem_t* pg = (m < 8) ? kA : kB;
@@ -172,13 +189,14 @@ struct TileBF16 {
     }
   }
 
-  // vA/vB: value page base for this kv head ([D][bs] elements).
+  // vA/vB: channel-0 value of the first token of half A / B (channels BS
+  // elements apart, [D][BS] pages).
   __device__ __forceinline__ static void load_v(V& v, const elem_t* vA, const elem_t* vB, int lane) {
     const int n = lane & 15, q = lane >> 4;
     const elem_t* pg = (q < 2) ? vA : vB;
-    const elem_t* base = pg + n * kPage + 8 * (q & 1);
+    const elem_t* base = pg + n * BS + 8 * (q & 1);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) v.v[dt] = ld16(base + dt * 16 * kPage);
+    for (int dt = 0; dt < DT; ++dt) v.v[dt] = ld16(base + dt * 16 * BS);
   }
 
   // row: query row base ([D] elements) or nullptr for a padding row.
@@ -241,14 +259,16 @@ struct TileBF16 {
 };
 
 // fp32 caches: v_mfma_f32_16x16x4_f32 (exact fp32 products).
-//  - Q.K^T: per page s, A row m = slot m; a 16-byte load gives channels
-//    16c + 4q .. +3, consumed by four products (k slot q <-> channel 16c+4q+i).
-//    Lane group q then holds tokens 16 s + 4q + j.
-//  - P.V: per page s and channel block, a 16-byte load of the channel-major
-//    page gives slots 4q .. 4q+3, consumed by four products (k slot q <-> slot
-//    4q + i), whose B operand is the lane's own score for that token.
-template <int D>
+//  - Q.K^T: per half s, A row m = token m of the half; a 16-byte load gives
+//    channels 16c + 4q .. +3, consumed by four products (k slot q <-> channel
+//    16c+4q+i).  Lane group q then holds tokens 16 s + 4q + j.
+//  - P.V: per half s and channel block, a 16-byte load of the channel-major
+//    page gives tokens 4q .. 4q+3 of the half, consumed by four products (k
+//    slot q <-> token 4q + i), whose B operand is the lane's own score for that
+//    token.
+template <int D, int BS>
 struct TileF32 {
+  static constexpr int kBS = BS;
   // Single-buffered tile loop: with the double-buffered loop and a work-group
   // stride of 4 tiles, fp32 head_dim 64 produced wrong results on gfx950 while
   // the single-buffered loop is exact; fp32 is the reference-precision path,
@@ -279,9 +299,9 @@ struct TileF32 {
     const int n = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const elem_t* base = (s ? vB : vA) + n * kPage + 4 * q;
+      const elem_t* base = (s ? vB : vA) + n * BS + 4 * q;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) v.v[s][dt] = *reinterpret_cast<const float4*>(base + dt * 16 * kPage);
+      for (int dt = 0; dt < DT; ++dt) v.v[s][dt] = *reinterpret_cast<const float4*>(base + dt * 16 * BS);
     }
   }
 

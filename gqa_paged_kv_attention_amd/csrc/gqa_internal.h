@@ -84,6 +84,7 @@ struct ReduceArgs {
   int num_kv_heads;
   int group;
   int max_blocks_per_seq;
+  int block_size;                   // tokens per page
   int max_partitions;
   int partition_size;
   int num_tokens;
@@ -105,17 +106,19 @@ struct CacheWriteArgs {
   int max_blocks_per_seq;
 };
 
-// kv_f32 / out_f32 select fp32 (true) or bf16 (false) storage.
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool kv_f32, bool out_f32, int num_seqs,
+// kv_f32 / out_f32 select fp32 (true) or bf16 (false) storage; block_size is
+// the page size in tokens (16, 32 or 64).
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs,
                          hipStream_t stream);
 // Workers (4 per work-group) that fill the device at full occupancy.
-int stream_workers(int head_dim, bool kv_f32, bool out_f32, int group, int num_seqs);
-hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream);
+int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs);
+hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                                hipStream_t stream);
 hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream);
 // Rows per prefill work-group (depends only on the build).
 int prefill_rows_per_group();
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool kv_f32, bool out_f32, int grid_groups,
-                          hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                          int grid_groups, hipStream_t stream);
 // Mixed batch, bf16: the scheduling pass writes the work units, ordered by
 // decreasing cost; the fused kernel runs unit i / Hkv for kv head i % Hkv.
 // Rows of a prefill unit (depends only on the build):
@@ -139,6 +142,7 @@ struct ScheduleArgs {
   int group;
   int rows_per_group;
   int max_blocks_per_seq;
+  int block_size;                   // tokens per page
   int partition_size;               // decode partitions (tokens, multiple of 32)
   int max_partitions;
   int causal;                       // as PrefillArgs::causal
@@ -150,8 +154,10 @@ struct MixedArgs {
   const int* unit_count;
 };
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream);
-hipError_t launch_mixed(const MixedArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream);
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,
+                        hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
-hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, int block_size, bool kv_f32,
+                              hipStream_t stream);
 
 }  // namespace gqa

@@ -33,8 +33,8 @@ namespace gqa {
 namespace {
 
 constexpr float kLazyRescale = 8.f;      // log2 growth of a row max before O is rescaled
-constexpr int kKeyTile = 64;             // keys per iteration: four pages
-constexpr int kTilePages = kKeyTile / kPage;
+constexpr int kKeyTile = 64;             // keys per iteration
+constexpr int kTileBlocks = kKeyTile / kHalf;   // 16-token blocks per tile, each inside one page
 
 template <int D, int NTW>
 struct PrefillLds {
@@ -48,7 +48,7 @@ struct PrefillLds {
   static constexpr int VBUF = D * VROW;             // one value buffer (elements)
   static constexpr int kBytes = 2 * (KBUF + VBUF) * 2;
   static constexpr int CH = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile, K and V each
-  // chunk i of a thread comes from page i * PI + (thread / (kThreads / PI)) of the tile
+  // chunk i of a thread comes from 16-token block i * PI + (thread / (kThreads / PI)) of the tile
   static constexpr int PI = 128 / D;
 };
 
@@ -65,59 +65,61 @@ struct PrefillLds {
 __device__ __forceinline__ int key_row(int t) { return t ^ ((t >> 2) & 4); }
 
 // This thread's share of a tile: for each 16-byte chunk of keys and of values,
-// its element offset inside its page and in the LDS tile.  The chunk's page is
-// wave-uniform: i * PI + pw.
-template <int D, int NTW>
+// its element offset from the first token of its 16-token block (key rows D
+// elements apart, value channels BS apart) and in the LDS tile.  The chunk's
+// block is wave-uniform: i * PI + pw.
+template <int D, int NTW, int BS>
 struct TileCopyPlan {
   typedef PrefillLds<D, NTW> S;
   int k_src[S::CH], k_dst[S::CH];
   int v_src[S::CH], v_dst[S::CH], v_tok[S::CH];
-  int pw;                                           // wave-uniform page offset of chunk 0
+  int pw;                                           // wave-uniform block offset of chunk 0
   __device__ __forceinline__ void init() {
     pw = S::PI == 1 ? 0 : uniform(threadIdx.x / (kThreads / S::PI));
 #pragma unroll
     for (int i = 0; i < S::CH; ++i) {
       const int ci = threadIdx.x + i * kThreads;
-      const int token = ci / (D / 8), col = ci % (D / 8);        // token / 16: page of chunk i
-      k_src[i] = (token % kPage) * D + col * 8;
+      const int token = ci / (D / 8), col = ci % (D / 8);        // token / 16: block of chunk i
+      k_src[i] = (token % kHalf) * D + col * 8;
       k_dst[i] = key_row(token) * S::KROW + col * 8;
-      const int h = ci / (2 * D), rem = ci % (2 * D);            // h: page of chunk i
+      const int h = ci / (2 * D), rem = ci % (2 * D);            // h: block of chunk i
       const int d = rem / 2, e = rem % 2;
-      v_src[i] = d * kPage + 8 * e;
+      v_src[i] = d * BS + 8 * e;
       v_dst[i] = d * S::VROW + 16 * h + 8 * e;
       v_tok[i] = 16 * h + 8 * e;                     // first token (in the tile) of this 8-token run
     }
   }
   // base pointer of chunk i (constant indices only, so TilePtrs stays in registers)
   template <class P>
-  __device__ __forceinline__ P page_of(int i, const P* pages) const {
-    if (S::PI == 1) return pages[i];
-    return pw ? pages[i * S::PI + 1] : pages[i * S::PI];
+  __device__ __forceinline__ P block_of(int i, const P* blocks) const {
+    if (S::PI == 1) return blocks[i];
+    return pw ? blocks[i * S::PI + 1] : blocks[i * S::PI];
   }
 };
 
-// Page base pointers (K and V, this kv head) of the four pages of a tile.
+// First-token pointers (K row, channel-0 value; this kv head) of the four
+// 16-token blocks of a tile.
 struct TilePtrs {
-  const uint16_t* k[kTilePages];
-  const uint16_t* v[kTilePages];
+  const uint16_t* k[kTileBlocks];
+  const uint16_t* v[kTileBlocks];
 };
 
-template <int D, int NTW>
-__device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW>& plan,
+template <int D, int NTW, int BS>
+__device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW, BS>& plan,
                                                const TilePtrs& tp) {
   typedef PrefillLds<D, NTW> S;
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) {
-    kreg[i] = ld16(plan.page_of(i, tp.k) + plan.k_src[i]);
-    vreg[i] = ld16(plan.page_of(i, tp.v) + plan.v_src[i]);
+    kreg[i] = ld16(plan.block_of(i, tp.k) + plan.k_src[i]);
+    vreg[i] = ld16(plan.block_of(i, tp.v) + plan.v_src[i]);
   }
 }
 
 // Registers -> LDS; values are converted to fp16, and with `tail` set those of
 // tokens at or past L become 0.
-template <int D, int NTW>
+template <int D, int NTW, int BS>
 __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const uint4* kreg, const uint4* vreg,
-                                               const TileCopyPlan<D, NTW>& plan, int tile_base, int L, bool tail) {
+                                               const TileCopyPlan<D, NTW, BS>& plan, int tile_base, int L, bool tail) {
   typedef PrefillLds<D, NTW> S;
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
@@ -149,15 +151,16 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 // kRowsPerGroup) of sequence b (new tokens [q0, q1), seq_lens[b] = seq_len)
 // against kv head kv.  Causal: token j sees keys up to seq_len - q_len + j;
 // otherwise (cross-attention) every row sees all seq_len keys, and q_len may
-// exceed seq_len.  sK / sV: two LDS buffers of KBUF and VBUF elements each.
-template <int D, int NTW, class OutT>
+// exceed seq_len.  Pages hold BS tokens.  sK / sV: two LDS buffers of KBUF
+// and VBUF elements each.
+template <int D, int NTW, int BS, class OutT>
 __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int q0, int q1, int seq_len, int kv,
                                              uint16_t* sK, uint16_t* sV) {
   typedef PrefillLds<D, NTW> S;
   const int G = a.group;
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0) return;
-  const int L = max(0, min(seq_len, a.max_blocks_per_seq * kPage));
+  const int L = clamp_len(seq_len, a.max_blocks_per_seq, BS);
   const int prior = L - q_len;
   if (a.causal && prior < 0) return;
   const int rows_total = q_len * G;
@@ -204,32 +207,35 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   const int group_hi = last_key(min(q_len - 1, (rt * S::kRowsPerGroup + S::kRowsPerGroup - 1) / G));
   // no tile when no key is visible (an empty encoder sequence): zero rows
   const int n_tiles = group_hi < 0 ? 0 : group_hi / kKeyTile + 1;
-  const int npages = (L + kPage - 1) / kPage;
+  const int npages = (L + BS - 1) / BS;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  const char* kc = reinterpret_cast<const char*>(a.key_cache) + (size_t)kv * (kPage * D * 2);
-  const char* vc = reinterpret_cast<const char*>(a.value_cache) + (size_t)kv * (kPage * D * 2);
-  const uint32_t page_bytes = (uint32_t)a.num_kv_heads * (kPage * D * 2);
+  const char* kc = reinterpret_cast<const char*>(a.key_cache) + (size_t)kv * (BS * D * 2);
+  const char* vc = reinterpret_cast<const char*>(a.value_cache) + (size_t)kv * (BS * D * 2);
+  const uint32_t page_bytes = (uint32_t)a.num_kv_heads * (BS * D * 2);
+  constexpr int kEntries = kKeyTile / BS;           // block-table entries per tile: 4, 2 or 1
 
-  TileCopyPlan<D, NTW> plan;
+  TileCopyPlan<D, NTW, BS> plan;
   plan.init();
   // Raw block-table entries of tile t (clamped to the last tile and page).
   // They are loaded one iteration before they are used, so that waiting for
   // them never waits for the K/V loads issued just before.
   auto fetch_pages = [&](int t, int* raw) {
-    const int pg = min(t, n_tiles - 1) * kTilePages;
+    const int pg = min(t, n_tiles - 1) * kEntries;
 #pragma unroll
-    for (int j = 0; j < kTilePages; ++j) raw[j] = bt[min(pg + j, npages - 1)];
+    for (int j = 0; j < kEntries; ++j) raw[j] = bt[min(pg + j, npages - 1)];
   };
+  // 16-token block j of the tile: entry j * 16 / BS, from token j * 16 mod BS of that page
   auto issue = [&](const int* raw, uint4* kr, uint4* vr) {
     TilePtrs tp;
 #pragma unroll
-    for (int j = 0; j < kTilePages; ++j) {
-      const uint32_t pid = (uint32_t)uniform((unsigned)raw[j] < (unsigned)a.num_blocks ? raw[j] : 0);
+    for (int j = 0; j < kTileBlocks; ++j) {
+      const int e = j * kHalf / BS, slot = j * kHalf % BS;
+      const uint32_t pid = (uint32_t)uniform((unsigned)raw[e] < (unsigned)a.num_blocks ? raw[e] : 0);
       const size_t off = (size_t)pid * page_bytes;
-      tp.k[j] = reinterpret_cast<const uint16_t*>(kc + off);
-      tp.v[j] = reinterpret_cast<const uint16_t*>(vc + off);
+      tp.k[j] = reinterpret_cast<const uint16_t*>(kc + off) + slot * D;
+      tp.v[j] = reinterpret_cast<const uint16_t*>(vc + off) + slot;
     }
-    load_tile_regs<D, NTW>(kr, vr, plan, tp);
+    load_tile_regs<D, NTW, BS>(kr, vr, plan, tp);
   };
 
   float m[NTW], mu[NTW];
@@ -247,12 +253,12 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   // to LDS buffer t & 1 at the top of iteration t - 1 and consumed in
   // iteration t, so each load has a whole iteration to arrive.
   uint4 kreg[S::CH], vreg[S::CH];
-  int raw[kTilePages];
+  int raw[kEntries];
   if (n_tiles > 0) {                     // uniform over the work-group
     fetch_pages(0, raw);
     issue(raw, kreg, vreg);
     fetch_pages(1, raw);
-    store_tile_lds<D, NTW>(sK, sV, kreg, vreg, plan, 0, L, kKeyTile > L);
+    store_tile_lds<D, NTW, BS>(sK, sV, kreg, vreg, plan, 0, L, kKeyTile > L);
     if (n_tiles > 1) issue(raw, kreg, vreg);
     fetch_pages(2, raw);
     __syncthreads();
@@ -261,7 +267,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   // LDS offsets of this lane's key rows (32-key half 0, products s = 0, 1;
   // token fed to row m as in TileBF16; half 1 is 32 rows further) and value
   // rows
-  const int kslot = ((n < 8) ? 0 : kPage) + (n & 3) + 8 * ((n >> 2) & 1);
+  const int kslot = ((n < 8) ? 0 : kHalf) + (n & 3) + 8 * ((n >> 2) & 1);
   const int koff0 = key_row(kslot) * S::KROW + 8 * q, koff1 = key_row(kslot + 4) * S::KROW + 8 * q;
   const int voff = n * S::VROW + 8 * q;
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0 x 8
@@ -357,7 +363,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
     // which every wave finished reading before the last barrier; then the
     // loads of tile it + 2, and the block-table entries of tile it + 3
     if (it + 1 < n_tiles)
-      store_tile_lds<D, NTW>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan, tb + kKeyTile, L,
+      store_tile_lds<D, NTW, BS>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan, tb + kKeyTile, L,
                              tb + 2 * kKeyTile > L);
     if (it + 2 < n_tiles) issue(raw, kreg, vreg);
     fetch_pages(it + 3, raw);
@@ -426,7 +432,7 @@ __device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* u
   *info = SeqInfo{q0, q1, sl};
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0 || q_len <= 0 || q_len > a.max_query_len) return false;
-  const int L = max(0, min(sl, a.max_blocks_per_seq * kPage));
+  const int L = clamp_len(sl, a.max_blocks_per_seq, a.block_size);
   if (q_len == 1) {
     const int Lp = min(L, a.max_partitions * a.partition_size);
     const int nparts = max(1, (Lp + a.partition_size - 1) / a.partition_size);
@@ -590,7 +596,7 @@ struct MixedLds {
   static constexpr int kBytes = kPrefillBytes > kDecodeBytes ? kPrefillBytes : kDecodeBytes;
 };
 
-template <int D, int NT, class OutT>
+template <int D, int NT, int BS, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void mixed_kernel(MixedArgs a) {
   typedef PrefillLds<D, kLdsNTW> S;
@@ -604,19 +610,19 @@ void mixed_kernel(MixedArgs a) {
   if (slot >= count) return;
   if (u.y >= 0) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-    prefill_unit<D, kLdsNTW, OutT>(a.prefill, u.x, u.y, u.z, u.w, seq_len, kv, sK, sK + 2 * S::KBUF);
+    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, seq_len, kv, sK, sK + 2 * S::KBUF);
   } else {
-    decode_partition_at<TileBF16<D>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, seq_len,
-                                                  reinterpret_cast<float*>(lds));
+    decode_partition_at<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, seq_len,
+                                                      reinterpret_cast<float*>(lds));
   }
 }
 
-template <int D, class OutT>
+template <int D, int BS, class OutT>
 hipError_t mixed_dispatch(const MixedArgs& a, int groups, hipStream_t s) {
   if (a.prefill.group <= 16)
-    hipLaunchKernelGGL((mixed_kernel<D, 1, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mixed_kernel<D, 1, BS, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((mixed_kernel<D, 2, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mixed_kernel<D, 2, BS, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -629,10 +635,16 @@ hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_mixed(const MixedArgs& a, int head_dim, bool out_f32, int grid_groups, hipStream_t stream) {
-  if (head_dim == 64)
-    return out_f32 ? mixed_dispatch<64, float>(a, grid_groups, stream) : mixed_dispatch<64, uint16_t>(a, grid_groups, stream);
-  return out_f32 ? mixed_dispatch<128, float>(a, grid_groups, stream) : mixed_dispatch<128, uint16_t>(a, grid_groups, stream);
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,
+                        hipStream_t stream) {
+  return with_block_size(block_size, [&](auto bs) {
+    constexpr int BS = decltype(bs)::value;
+    if (head_dim == 64)
+      return out_f32 ? mixed_dispatch<64, BS, float>(a, grid_groups, stream)
+                     : mixed_dispatch<64, BS, uint16_t>(a, grid_groups, stream);
+    return out_f32 ? mixed_dispatch<128, BS, float>(a, grid_groups, stream)
+                   : mixed_dispatch<128, BS, uint16_t>(a, grid_groups, stream);
+  });
 }
 
 }  // namespace gqa

@@ -5,7 +5,8 @@
 // sequence b is the sequence's position seq_lens[b] - q_len + j; it lands in
 // page block_tables[b][pos / bs] at slot pos % bs.  Keys go to the token-major
 // key page ([bs][d]); values to the channel-major value page ([d][bs]).  The
-// copy moves bit patterns, so it is exact for any storage dtype.
+// copy moves bit patterns, so it is exact for any storage dtype.  Pages hold
+// bs = 16, 32 or 64 tokens.
 #include "gqa_common.h"
 #include "gqa_internal.h"
 
@@ -23,7 +24,7 @@ constexpr int kLdsSeqs = 4095;          // query_start_loc staged in LDS up to t
 // guess fails does it search query_start_loc (staged in LDS by the work-group
 // when the batch is small enough, else in memory).  The work-group-wide
 // staging therefore sits behind a uniform branch that decode steps skip.
-template <int D, class T>
+template <int D, int BS, class T>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CH = D / VEC;
@@ -69,35 +70,40 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
   if (!active) return;
   if (tok < q0 || tok >= q1) return;
   const int pos = len - (q1 - q0) + (tok - q0);
-  if (pos < 0 || pos >= a.max_blocks_per_seq * kPage) return;
-  const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kPage];
+  if (pos < 0 || pos >= a.max_blocks_per_seq * BS) return;
+  const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / BS];
   if ((unsigned)page >= (unsigned)a.num_blocks) return;
-  const int slot = pos % kPage;
+  const int slot = pos % BS;
 
-  const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)(kPage * D);
+  const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)(BS * D);
   *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.key_cache) + pbase + (size_t)slot * D + c * VEC) = kx;
   T vals[VEC];
   __builtin_memcpy(vals, &vx, 16);
-  T* vdst = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)(c * VEC) * kPage + slot;
+  T* vdst = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)(c * VEC) * BS + slot;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) vdst[(size_t)e * kPage] = vals[e];
+  for (int e = 0; e < VEC; ++e) vdst[(size_t)e * BS] = vals[e];
 }
 
 template <class T>
-hipError_t dispatch(const CacheWriteArgs& a, int D, hipStream_t s) {
+hipError_t dispatch(const CacheWriteArgs& a, int D, int block_size, hipStream_t s) {
   const long long total = (long long)a.num_tokens * a.num_kv_heads * (D * (long long)sizeof(T) / 16);
   const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
-  if (D == 64)
-    hipLaunchKernelGGL((cache_write_kernel<64, T>), dim3(blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((cache_write_kernel<128, T>), dim3(blocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return with_block_size(block_size, [&](auto bs) {
+    constexpr int BS = decltype(bs)::value;
+    if (D == 64)
+      hipLaunchKernelGGL((cache_write_kernel<64, BS, T>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<128, BS, T>), dim3(blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
 
-hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, bool kv_f32, hipStream_t stream) {
-  return kv_f32 ? dispatch<float>(a, head_dim, stream) : dispatch<uint16_t>(a, head_dim, stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, int block_size, bool kv_f32,
+                              hipStream_t stream) {
+  return kv_f32 ? dispatch<float>(a, head_dim, block_size, stream)
+                : dispatch<uint16_t>(a, head_dim, block_size, stream);
 }
 
 }  // namespace gqa

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(ReduceArgs a) {
     if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
     row = q0;
   }
-  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * kPage));
+  const int L = max(0, min(a.seq_lens[b], a.max_blocks_per_seq * a.block_size));
   const int n = min((L + a.partition_size - 1) / a.partition_size, a.max_partitions);
   if (a.skip_single && n <= 1) return;
   const size_t hb = (size_t)b * a.num_heads + h;

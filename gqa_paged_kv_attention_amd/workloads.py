@@ -246,12 +246,13 @@ def tiny_decode(seed: int = 1, **kw) -> PagedBatch:
                       seq_lens=ctx, query_lens=np.ones(4, np.int32), dtype=F32, scale=1.0 / 8.0, rng=rng, **kw)
 
 
-def llama31_8b_decode(seed: int = 2, num_seqs: int = 64, ctx_lo: int = 512, ctx_hi: int = 4096, **kw) -> PagedBatch:
-    """Llama-3.1-8B decode: Hq=32, Hkv=8, d=128, block 16, bf16, context U{512..4096}."""
+def llama31_8b_decode(seed: int = 2, num_seqs: int = 64, ctx_lo: int = 512, ctx_hi: int = 4096,
+                      block_size: int = 16, **kw) -> PagedBatch:
+    """Llama-3.1-8B decode: Hq=32, Hkv=8, d=128, block 16 (or block_size), bf16, context U{512..4096}."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(ctx_lo, ctx_hi + 1, size=num_seqs)
     return make_batch(name="llama31_8b_decode", seed=seed, num_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, seq_lens=ctx, query_lens=np.ones(num_seqs, np.int32), dtype=BF16,
+                      block_size=block_size, seq_lens=ctx, query_lens=np.ones(num_seqs, np.int32), dtype=BF16,
                       rng=rng, **kw)
 
 

@@ -41,7 +41,11 @@
  *
  * The value page is stored head_dim-major (tokens of a page contiguous per
  * channel) so that the P.V matrix-core operand is a plain 16-byte load; the key
- * page is token-major for the same reason on the Q.K^T side.
+ * page is token-major for the same reason on the Q.K^T side.  Pages of 16, 32
+ * or 64 tokens are supported by every call; the kernels' key tiles do not
+ * depend on the page size ("[Performance] Use optimized kernels for MQA/GQA",
+ * thread: a paged kernel that required the page size to equal its key tile),
+ * and the same tokens give the same results in any of them.
  *
  * Device-data preconditions (not checked on the host; the kernels clamp so that
  * a violation gives a wrong result, never an out-of-bounds access):
@@ -78,7 +82,7 @@ typedef struct {
   int32_t num_heads;           /* Hq */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;            /* d: 64 or 128 */
-  int32_t block_size;          /* tokens per page: 16 */
+  int32_t block_size;          /* tokens per page: 16, 32 or 64 */
   int32_t num_blocks;          /* pages in each cache */
   int32_t max_blocks_per_seq;  /* row stride of block_tables */
   gqa_dtype q_dtype;           /* query (and key/value of reshape_and_cache) */

@@ -2,6 +2,8 @@
 through its C ABI (via the ctypes binding), and compare with the oracle."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -91,3 +93,31 @@ def poison_tails(bt: wl.PagedBatch):
         page = bt.block_tables[b][n - 1]
         bt.key_cache[page, :, used:, :] = nan
         bt.value_cache[page, :, :, used:] = nan
+
+
+def repage(bt: wl.PagedBatch, block_size: int, seed: int = 0) -> wl.PagedBatch:
+    """The same batch (queries, new K/V, lengths and every cached token's
+    values) stored in pages of `block_size` tokens under a fresh seeded page
+    permutation.  A layout copy only: slack pages and page tails hold NaN."""
+    nan = np.uint16(0x7FC0) if bt.dtype == wl.BF16 else np.float32("nan")
+    B, Hkv, d = bt.num_seqs, bt.num_kv_heads, bt.head_dim
+    pages = (bt.seq_lens.astype(np.int64) + block_size - 1) // block_size
+    used = int(pages.sum())
+    num_blocks = used + max(1, used // 10)
+    perm = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
+    max_blocks = max(1, -(-bt.max_blocks_per_seq * bt.block_size // block_size))
+    tables = np.full((B, max_blocks), perm[used:][0], dtype=np.int32)
+    kc = np.full((num_blocks, Hkv, block_size, d), nan, dtype=bt.key_cache.dtype)
+    vc = np.full((num_blocks, Hkv, d, block_size), nan, dtype=bt.value_cache.dtype)
+    off = 0
+    for b in range(B):
+        L, n = int(bt.seq_lens[b]), int(pages[b])
+        tables[b, :n] = perm[off:off + n]
+        off += n
+        t = np.arange(L)
+        src_pg = bt.block_tables[b][t // bt.block_size]
+        dst_pg = tables[b][t // block_size]
+        kc[dst_pg, :, t % block_size, :] = bt.key_cache[src_pg, :, t % bt.block_size, :]
+        vc[dst_pg, :, :, t % block_size] = bt.value_cache[src_pg, :, :, t % bt.block_size]
+    return dataclasses.replace(bt, block_size=block_size, block_tables=tables, num_blocks=num_blocks,
+                               slack_pages=np.sort(perm[used:]), key_cache=kc, value_cache=vc)

@@ -50,13 +50,22 @@ def decode(lib, d, max_seq_len=256, partition=0, ws=None, wsb=0, ptr=FAKE, scale
     (dict(num_kv_heads=7), INVALID),
     (dict(num_heads=0), INVALID),
     (dict(head_dim=96), UNSUPPORTED),
-    (dict(block_size=32), UNSUPPORTED),
+    (dict(block_size=8), UNSUPPORTED),
+    (dict(block_size=48), UNSUPPORTED),
+    (dict(block_size=128), UNSUPPORTED),
     (dict(q_dtype=ops.GQA_F32), UNSUPPORTED),
     (dict(out_dtype=7), INVALID),
     (dict(num_heads=64, num_kv_heads=1), UNSUPPORTED),       # group of 64 > 32
 ])
 def test_decode_rejects_bad_dims(lib, kw, expect):
     assert decode(lib, dims(**kw)) == expect
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+def test_page_sizes_accepted(lib, bs):
+    # past the dims check, a missing workspace is reported
+    assert decode(lib, dims(block_size=bs, max_blocks_per_seq=4096 // bs), max_seq_len=4096, partition=512) == \
+        WORKSPACE
 
 
 def test_decode_rejects_null_pointer_and_bad_partition(lib):
