@@ -39,7 +39,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "0a2b4915b5648e17ee243a2143e0061c32c18f1276b9384bf91d0963a9078b53", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648796378, "write_bytes_per_call": 6338613, "hbm_bytes_per_call": 655134992, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "8ef5df7c17ec633043612a0102530c877b5957559d2783a5bf9146609bb66608", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645957480, "write_bytes_per_call": 6333802, "hbm_bytes_per_call": 652291282, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():

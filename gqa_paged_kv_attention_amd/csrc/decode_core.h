@@ -88,17 +88,6 @@ __device__ __forceinline__ void load_group_query(typename Tile::Q qf[NT], const 
   }
 }
 
-// Walk tiles it0, it0+step, ... < it1 of one (sequence, kv head); tile i covers
-// keys [32 i, 32 i + 32).  Keys past `lim` are masked; values of tokens at or
-// past L are zeroed so that whatever sits in the pool beyond the sequence
-// (including NaN) cannot reach the output.
-//
-// Software pipelining: two register sets (A, B) alternate, and the loads of
-// the next tile are issued before the current tile is computed, so a wave
-// always has a tile in flight.  The prefetch is unconditional (its tile index
-// is clamped to the last tile, whose re-read hits in cache), which keeps the
-// load count per iteration fixed and lets the compiler wait on just the
-// current tile's loads.
 // Pages of tile `it`: with 16-token pages the two halves are pages 2 it and
 // 2 it + 1 (the second clamped to the last page); with 32- or 64-token pages
 // both halves sit in page 32 it / BS, from token (32 it) mod BS on.
@@ -118,6 +107,10 @@ struct TilePages {
     }
   }
 };
+
+// A wave that walks consecutive tiles loads them in pairs (see run_tiles).
+template <class Tile>
+constexpr bool kPairedTiles = Tile::kPipelined;
 
 template <class Tile, int D>
 __device__ __forceinline__ void load_tile(typename Tile::K& kf, typename Tile::V& vf, const TilePages<Tile, D>& pg,
@@ -152,6 +145,19 @@ __device__ __forceinline__ void compute_tile(WaveState<Tile, NT>& st, const type
   }
 }
 
+// Walk tiles it0, it0+step, ... < it1 of one (sequence, kv head); tile i covers
+// keys [32 i, 32 i + 32).  Keys past `lim` are masked; values of tokens at or
+// past L are zeroed so that whatever sits in the pool beyond the sequence
+// (including NaN) cannot reach the output.
+//
+// Two register sets (A, B).  A wave that walks consecutive tiles (step 1)
+// loads them in pairs, then computes both.  Otherwise (tiles shared round-
+// robin by the waves of a work-group) the sets alternate: the loads of the
+// next tile are issued before the current tile is computed, so a wave always
+// has a tile in flight.  Prefetches are unconditional (the tile index is
+// clamped to the last tile, whose re-read hits in cache), which keeps the load
+// count per iteration fixed and lets the compiler wait on just the tile about
+// to be computed.
 template <class Tile, int D, int NT>
 __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typename Tile::Q qf[NT], const void* kc,
                                           const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
@@ -172,6 +178,29 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
   const int last = it0 + (it1 - 1 - it0) / step * step;     // last tile this wave visits
   typename Tile::K kA, kB;
   typename Tile::V vA, vB;
+  if constexpr (kPairedTiles<Tile>) {
+    if (step == 1) {
+      // Tiles in pairs: both tiles' loads are issued together, then both are
+      // computed, so a wave has 64 tokens of K and V in flight at once.  With
+      // 64-token pages the pair is one page and the two halves of every value
+      // line are requested together (one tile at a time, L2 evicted most lines
+      // before the second half was asked for: +34% HBM reads).  The page ids
+      // of the next pair are loaded while this pair is computed; a pair past
+      // the end repeats the last tile, whose result is not used.
+      TilePages<Tile, D> pa, pb;
+      pa.fetch(bt, it0, npages, num_blocks);
+      pb.fetch(bt, min(it0 + 1, last), npages, num_blocks);
+      for (int it = it0; it < it1; it += 2) {
+        load_tile<Tile, D>(kA, vA, pa, kc, vc, num_kv_heads, kv, lane);
+        load_tile<Tile, D>(kB, vB, pb, kc, vc, num_kv_heads, kv, lane);
+        pa.fetch(bt, min(it + 2, last), npages, num_blocks);
+        pb.fetch(bt, min(it + 3, last), npages, num_blocks);
+        compute_tile<Tile, NT>(st, qf, kA, vA, it * kTile, L, lim, scale_log2, lane);
+        if (it + 1 < it1) compute_tile<Tile, NT>(st, qf, kB, vB, (it + 1) * kTile, L, lim, scale_log2, lane);
+      }
+      return;
+    }
+  }
   TilePages<Tile, D> pg;
   pg.fetch(bt, it0, npages, num_blocks);
   load_tile<Tile, D>(kA, vA, pg, kc, vc, num_kv_heads, kv, lane);
