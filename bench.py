@@ -10,7 +10,8 @@ Metric: effective KV GB/s = sum(seq_len) * 2 * Hkv * d * 2 bytes / step time.
 Also reported: the decode kernel's roofline (HIP events on its launch
 stream), the mixed chunked-prefill + decode batch's tokens/s, the GQA saving
 against the same cache expanded per query head, cross-attention over a static
-encoder cache, and the CPU oracle's throughput on a bounded sample as a
+encoder cache, the decode per page size, the shared-prefix decode against the
+plain decode, and the CPU oracle's throughput on a bounded sample as a
 baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
@@ -55,6 +56,7 @@ def parse():
     ap.add_argument("--no-gqa-comparison", action="store_true")
     ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention leg")
     ap.add_argument("--no-page-sizes", action="store_true", help="skip the 16/32/64-token page comparison")
+    ap.add_argument("--no-shared-prefix", action="store_true", help="skip the shared-prefix decode comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -231,6 +233,57 @@ def page_size_leg(dev, stream, reps, seed):
     return res
 
 
+def shared_prefix_leg(dev, stream, reps):
+    """Groups of sequences sharing a prompt prefix (prefix-cached pages): the
+    plain decode over the aliased block tables, the shared-prefix decode, and
+    the plain decode over private copies of the prefix, on the same tokens."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    res = {"workload": "shared_prefix_decode (groups of sequences sharing a prompt, suffixes U{16..512}, "
+                       "Hq=32, Hkv=8, d=128, bf16)"}
+    for groups, size, prefix in ((4, 16, 2048), (4, 64, 4096)):
+        bt, gs, pl = wl.shared_prefix_decode(seed=7, num_groups=groups, group_size=size, prefix_len=prefix)
+        up = lambda a: ops.to_device(a, dev)
+        q, kc, vc, tb, sl, dgs, dpl = (up(x) for x in (bt.query, bt.key_cache, bt.value_cache, bt.block_tables,
+                                                        bt.seq_lens, gs, pl))
+        out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tb,
+                             q_dtype=q.dtype, out_dtype=out.dtype)
+        ws = torch.zeros(max(ops.shared_prefix_workspace_size(dims, groups, size, bt.max_seq_len, 0),
+                             ops.decode_workspace_size(dims, bt.max_seq_len, 0), 1), dtype=torch.uint8, device=dev)
+        plain = lambda: ops.paged_gqa_decode(q, kc, vc, tb, sl, bt.max_seq_len, bt.scale, out=out, workspace=ws)
+        shared = lambda: ops.paged_gqa_decode_shared_prefix(q, kc, vc, tb, sl, dgs, dpl, size, bt.max_seq_len,
+                                                            bt.scale, out=out, workspace=ws)
+        times = {}
+        for name, f in (("plain_aliased", plain), ("shared_prefix", shared)):
+            for _ in range(3):
+                f()
+            times[name] = event_time_ms(f, reps, stream)
+        o_shared = out.clone()
+        plain()
+        torch.cuda.synchronize()
+        max_diff = float((out - o_shared).abs().max())
+        # every sequence with pages of its own: a batch of the same lengths without aliasing
+        bt2 = wl.make_batch(name="private", seed=7, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                            seq_lens=bt.seq_lens, query_lens=bt.query_lens, dtype=bt.dtype)
+        kc2, vc2, tb2 = up(bt2.key_cache), up(bt2.value_cache), up(bt2.block_tables)
+        private = lambda: ops.paged_gqa_decode(q, kc2, vc2, tb2, sl, bt.max_seq_len, bt.scale, out=out, workspace=ws)
+        for _ in range(3):
+            private()
+        times["plain_private"] = event_time_ms(private, reps, stream)
+        unique = (prefix * groups + int(bt.seq_lens.sum()) - prefix * bt.num_seqs) * bt.num_kv_heads * 512
+        res[f"g{groups}x{size}_p{prefix}"] = {
+            "us": {k: round(v * 1e3, 2) for k, v in times.items()},
+            "speedup_vs_aliased": round(times["plain_aliased"] / times["shared_prefix"], 2),
+            "unique_kv_bytes": unique, "logical_kv_bytes": bt.kv_bytes(),
+            "unique_gbs_shared": round(unique / (times["shared_prefix"] * 1e-3) / 1e9, 1),
+            "max_abs_diff_vs_plain": max_diff}
+        del q, kc, vc, kc2, vc2, out, ws
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -344,6 +397,9 @@ def main():
 
     if not args.no_page_sizes:
         record["page_sizes"] = page_size_leg(dev, stream, 50, args.seed)
+
+    if not args.no_shared_prefix:
+        record["shared_prefix"] = shared_prefix_leg(dev, stream, 30)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)

@@ -364,6 +364,51 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
                     max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
 }
 
+// Shared-prefix decode (bf16).  Each role is cut to give about
+// kSharedUnits work-groups (two per CU): prefix chunks of 512..2048 keys
+// (whole 64-key tiles) over num_groups x row tiles x Hkv; suffix partitions of
+// partition_size tokens, or, when the library picks, of at least 256 tokens
+// over num_seqs x Hkv.  max_seq_len bounds both the prefixes and the suffixes.
+constexpr long long kSharedUnits = 512;
+
+struct SharedPrefixPlan {
+  int row_tiles, chunk_tokens, prefix_chunks, suffix_parts, suffix_psize, slots;
+  size_t out_bytes, lse_bytes, meta_bytes;
+  long long groups;
+};
+
+int round_up(long long x, int m) { return (int)((x + m - 1) / m * m); }
+
+bool shared_prefix_plan(const gqa_dims& d, int32_t num_groups, int32_t max_group_size, int32_t max_seq_len,
+                        int32_t partition_size, SharedPrefixPlan* pl) {
+  if (num_groups < 0 || max_group_size < 0 || max_group_size > d.num_seqs) return false;
+  if (max_seq_len < 0 || max_seq_len > kMaxSeqLen || partition_size < 0 || partition_size % kTileTokens) return false;
+  const int G = d.num_heads / d.num_kv_heads;
+  const long long len = std::max(1, max_seq_len);
+  pl->row_tiles = (int)(((long long)max_group_size * G + gqa::prefill_lds_rows_per_group() - 1) /
+                        gqa::prefill_lds_rows_per_group());
+  const long long chunk_units = std::max(1LL, (long long)num_groups * pl->row_tiles * d.num_kv_heads);
+  const long long chunks_goal = std::max(1LL, (kSharedUnits + chunk_units - 1) / chunk_units);
+  pl->chunk_tokens = std::min(2048, std::max(512, round_up((len + chunks_goal - 1) / chunks_goal, 64)));
+  pl->prefix_chunks = (int)((len + pl->chunk_tokens - 1) / pl->chunk_tokens);
+  if (partition_size > 0) {
+    pl->suffix_psize = partition_size;
+  } else {
+    const long long seq_units = std::max(1LL, (long long)d.num_seqs * d.num_kv_heads);
+    const long long parts_goal = std::max(1LL, (kSharedUnits + seq_units - 1) / seq_units);
+    pl->suffix_psize = std::max(256, round_up((len + parts_goal - 1) / parts_goal, kTileTokens));
+  }
+  pl->suffix_parts = (int)((len + pl->suffix_psize - 1) / pl->suffix_psize);
+  pl->slots = pl->prefix_chunks + pl->suffix_parts;
+  const size_t rows = (size_t)d.num_seqs * d.num_heads * pl->slots;
+  pl->out_bytes = align_up(rows * d.head_dim * sizeof(float));
+  pl->lse_bytes = align_up(rows * sizeof(float));
+  pl->meta_bytes = align_up((size_t)d.num_seqs * 2 * sizeof(int));
+  pl->groups = (long long)num_groups * pl->row_tiles * pl->prefix_chunks * d.num_kv_heads +
+               (long long)d.num_seqs * pl->suffix_parts * d.num_kv_heads;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -485,6 +530,96 @@ int32_t paged_cross_attention(void* out, const void* query, const void* key_cach
   return run_mixed(out, query, key_cache, value_cache, block_tables, encoder_lens, query_start_loc, num_tokens,
                    max_query_len, max_encoder_len, dims, scale, partition_size, workspace, workspace_bytes,
                    reinterpret_cast<hipStream_t>(stream), false);
+}
+
+size_t paged_gqa_decode_shared_prefix_workspace_size(gqa_dims dims, int32_t num_groups, int32_t max_group_size,
+                                                    int32_t max_seq_len, int32_t partition_size) {
+  if (check_dims(dims) != GQA_OK) return 0;
+  if (dims.kv_dtype == GQA_F32) return decode_workspace(dims, max_seq_len, partition_size);
+  SharedPrefixPlan pl;
+  if (!shared_prefix_plan(dims, num_groups, max_group_size, max_seq_len, partition_size, &pl)) return 0;
+  return pl.out_bytes + pl.lse_bytes + pl.meta_bytes;
+}
+
+int32_t paged_gqa_decode_shared_prefix(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       const int32_t* group_start, const int32_t* prefix_lens, int32_t num_groups,
+                                       int32_t max_group_size, int32_t max_seq_len, gqa_dims dims, float scale,
+                                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dims.kv_dtype == GQA_F32) {
+    // fp32 caches: the plain decode (each sequence reads its own pages)
+    if (dims.num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens))
+      return GQA_ERR_INVALID_ARG;
+    return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
+                      max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
+  }
+  SharedPrefixPlan pl;
+  if (!shared_prefix_plan(dims, num_groups, max_group_size, max_seq_len, partition_size, &pl))
+    return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs == 0) return GQA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens) return GQA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!group_start || !prefix_lens)) return GQA_ERR_INVALID_ARG;
+  if (pl.groups >= 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < pl.out_bytes + pl.lse_bytes + pl.meta_bytes) return GQA_ERR_WORKSPACE;
+  const int G = dims.num_heads / dims.num_kv_heads;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  char* ws = reinterpret_cast<char*>(workspace);
+
+  gqa::SharedPrefixArgs a;
+  gqa::PrefillArgs& p = a.prefill;
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.query_start_loc = nullptr;
+  p.num_seqs = dims.num_seqs;
+  p.num_heads = dims.num_heads;
+  p.num_kv_heads = dims.num_kv_heads;
+  p.group = G;
+  p.num_blocks = dims.num_blocks;
+  p.max_blocks_per_seq = dims.max_blocks_per_seq;
+  p.num_tokens = dims.num_seqs;
+  p.scale_log2 = scale_log2;
+  p.causal = 0;
+  gqa::DecodeArgs& d = a.decode;
+  d.out = out;
+  d.query = query;
+  d.key_cache = key_cache;
+  d.value_cache = value_cache;
+  d.block_tables = block_tables;
+  d.seq_lens = seq_lens;
+  d.query_start_loc = nullptr;
+  d.partial_out = nullptr;
+  d.partial_lse = nullptr;
+  d.num_heads = dims.num_heads;
+  d.num_kv_heads = dims.num_kv_heads;
+  d.group = G;
+  d.num_blocks = dims.num_blocks;
+  d.max_blocks_per_seq = dims.max_blocks_per_seq;
+  d.num_tokens = dims.num_seqs;
+  d.partition_size = pl.suffix_psize;
+  d.max_partitions = pl.suffix_parts;
+  d.scale_log2 = scale_log2;
+  a.group_start = group_start;
+  a.prefix_lens = prefix_lens;
+  a.part_out = reinterpret_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(ws + pl.out_bytes);
+  a.seq_meta = reinterpret_cast<int2*>(ws + pl.out_bytes + pl.lse_bytes);
+  a.num_seqs = dims.num_seqs;
+  a.num_groups = num_groups;
+  a.row_tiles = pl.row_tiles;
+  a.prefix_chunks = pl.prefix_chunks;
+  a.chunk_tokens = pl.chunk_tokens;
+  a.slots = pl.slots;
+  return status_from(gqa::launch_shared_prefix(a, dims.head_dim, dims.block_size, dims.out_dtype == GQA_F32, s));
 }
 
 }  // extern "C"

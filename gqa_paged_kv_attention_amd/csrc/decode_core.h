@@ -248,12 +248,25 @@ struct DecodeMergeLds {
   static constexpr int kFloats = kWaves * R * (2 + D + 4);
 };
 
+// Where a unit that covers part of a row's keys writes: each row's
+// normalised partial output and its natural-log log-sum-exp, in slot `slot`
+// (plus the unit's partition index, for decode partitions) of `slots` per
+// (row, head).
+struct UnitOut {
+  float* part_out = nullptr;               // [rows, Hq, slots, D]
+  float* part_lse = nullptr;               // [rows, Hq, slots]
+  int slot = 0, slots = 1;
+};
+
 // Partition p of (sequence b, kv head kv), run by the 4 waves of a work-group,
 // for query row `row` and seq_lens[b] = seq_len; `lds` holds
-// DecodeMergeLds<D, NT>::kFloats floats.
+// DecodeMergeLds<D, NT>::kFloats floats.  Partitions cover keys [k_begin, L)
+// (k_begin a multiple of 32).  With `uo`, every partition writes a partial to
+// uo's slots; otherwise a single partition writes `out` and several write
+// a.partial_out / a.partial_lse.
 template <class Tile, int D, int NT, class OutT>
 __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, int kv, int b, int row, int seq_len,
-                                                    float* lds) {
+                                                    float* lds, int k_begin = 0, const UnitOut* uo = nullptr) {
   constexpr int R = NT * 16;            // padded rows of the group
   const int G = a.group;
   const int lane = lane_id(), w = wave_id();
@@ -262,22 +275,22 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   typename Tile::Q qf[NT];
   load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
 
-  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq, Tile::kBS), a.max_partitions * a.partition_size);
-  const int nparts = (L + a.partition_size - 1) / a.partition_size;
+  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq, Tile::kBS), k_begin + a.max_partitions * a.partition_size);
+  const int nparts = L > k_begin ? (L - k_begin + a.partition_size - 1) / a.partition_size : 0;
   OutT* out = reinterpret_cast<OutT*>(a.out);
 
-  if (L == 0) {
-    if (p == 0)
+  if (nparts == 0) {
+    if (p == 0 && !uo)
       for (int i = threadIdx.x; i < G * D; i += kThreads)
         store1(out + ((size_t)row * a.num_heads + kv * G) * D + i, 0.f);
     return;
   }
   if (p >= nparts) return;
 
-  // equal split of the sequence's tiles over its partitions (each gets >= 1 tile)
-  const int tiles_all = (L + kTile - 1) / kTile;
+  // equal split of the range's tiles over its partitions (each gets >= 1 tile)
+  const int tiles_all = (L - k_begin + kTile - 1) / kTile;
   const int per = tiles_all / nparts, extra = tiles_all % nparts;
-  const int tile0 = p * per + min(p, extra);
+  const int tile0 = k_begin / kTile + p * per + min(p, extra);
   const int n_tiles = per + (p < extra ? 1 : 0);
   const int t1 = min((tile0 + n_tiles) * kTile, L);
 
@@ -321,22 +334,28 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   __syncthreads();
 
   const size_t head0 = (size_t)b * a.num_heads + kv * G;
+  // partial slot of row r: [(head0 + r) * stride + slot]
+  const bool partial = uo || nparts > 1;
+  float* part_out = uo ? uo->part_out : a.partial_out;
+  float* part_lse = uo ? uo->part_lse : a.partial_lse;
+  const int stride = uo ? uo->slots : a.max_partitions;
+  const int slot = uo ? uo->slot + p : p;
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int r = i / D, d = i % D;
     const float v = sm_o[0][r][d] + sm_o[1][r][d] + sm_o[2][r][d] + sm_o[3][r][d];
-    if (nparts == 1)
+    if (!partial)
       store1(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
     else
-      a.partial_out[((head0 + r) * a.max_partitions + p) * D + d] = v;
+      part_out[((head0 + r) * stride + slot) * D + d] = v;
   }
-  if (nparts > 1 && threadIdx.x < G) {
+  if (partial && threadIdx.x < G) {
     const int r = threadIdx.x;
     float M = -INFINITY;
     for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][r]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ls = 0.f;
     for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
-    a.partial_lse[(head0 + r) * a.max_partitions + p] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+    part_lse[(head0 + r) * stride + slot] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
   }
 }
 

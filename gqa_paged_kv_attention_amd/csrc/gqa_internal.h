@@ -153,6 +153,30 @@ struct MixedArgs {
   const MixedUnit* units;
   const int* unit_count;
 };
+// Shared-prefix decode, bf16: groups of consecutive sequences whose first
+// prefix_lens[g] tokens are the same.  Prefix units (group, row tile, key
+// chunk, kv head) run the prefill role over the group's queries against the
+// shared keys [chunk * PC, ...) of the first member's block table; suffix
+// units (sequence, partition, kv head) run the decode over the sequence's
+// remaining keys.  Both write partials, merged per (sequence, head).
+struct SharedPrefixArgs {
+  PrefillArgs prefill;              // query rows = sequences, causal = 0
+  DecodeArgs decode;                // suffix partitions of partition_size tokens
+  const int32_t* group_start;       // [num_groups + 1]
+  const int32_t* prefix_lens;       // [num_groups]
+  float* part_out;                  // [B, Hq, slots, D]
+  float* part_lse;                  // [B, Hq, slots]
+  int2* seq_meta;                   // [B]: {prefix chunks, suffix partitions}
+  int num_seqs;
+  int num_groups;
+  int row_tiles;                    // row tiles of the largest group
+  int prefix_chunks;                // MC: chunk slots [0, MC)
+  int chunk_tokens;                 // PC, a multiple of 64
+  int slots;                        // MC + suffix partitions
+};
+hipError_t launch_shared_prefix(const SharedPrefixArgs& a, int head_dim, int block_size, bool out_f32,
+                                hipStream_t stream);
+
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream);
 hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,
                         hipStream_t stream);

@@ -69,6 +69,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_cross_attention_workspace_size.restype = sz
     lib.paged_cross_attention.argtypes = list(lib.chunked_prefill_paged_decode.argtypes)
     lib.paged_cross_attention.restype = i32
+    lib.paged_gqa_decode_shared_prefix_workspace_size.argtypes = [Dims, i32, i32, i32, i32]
+    lib.paged_gqa_decode_shared_prefix_workspace_size.restype = sz
+    lib.paged_gqa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, Dims, f32, i32,
+                                                   vp, sz, vp]
+    lib.paged_gqa_decode_shared_prefix.restype = i32
     _lib = lib
     return lib
 
@@ -119,7 +124,7 @@ def _check_device(*ts):
 def _check_int32(*ts):
     for t in ts:
         if t is not None and t.dtype != torch.int32:
-            raise TypeError("block_tables, seq_lens and query_start_loc must be int32")
+            raise TypeError("block tables, lengths and index arrays must be int32")
 
 
 def make_dims(*, num_seqs, num_heads, key_cache, block_tables, q_dtype, out_dtype) -> Dims:
@@ -262,6 +267,39 @@ def paged_cross_attention(query, key_cache, value_cache, block_tables, encoder_l
                                     _ptr(encoder_lens), _ptr(query_start_loc), T, int(max_query_len),
                                     int(max_encoder_len), dims, float(scale), int(partition_size), _ptr(ws), wsb,
                                     _stream(stream)))
+    return out
+
+
+def shared_prefix_workspace_size(dims: Dims, num_groups: int, max_group_size: int, max_seq_len: int,
+                                 partition_size: int) -> int:
+    return int(load_library().paged_gqa_decode_shared_prefix_workspace_size(
+        dims, int(num_groups), int(max_group_size), int(max_seq_len), int(partition_size)))
+
+
+def paged_gqa_decode_shared_prefix(query, key_cache, value_cache, block_tables, seq_lens, group_start, prefix_lens,
+                                   max_group_size: int, max_seq_len: int, scale: float, partition_size: int = 0,
+                                   out=None, out_dtype=None, workspace=None, stream=None):
+    """Decode ``query [B, Hq, d]`` -> ``out [B, Hq, d]`` where the sequences of group g
+    (``group_start[g] .. group_start[g+1]-1``) share their first ``prefix_lens[g]`` tokens."""
+    lib = load_library()
+    _check_device(query, key_cache, value_cache, block_tables, seq_lens, group_start, prefix_lens, out, workspace)
+    _check_int32(block_tables, seq_lens, group_start, prefix_lens)
+    B, Hq, d = query.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=B, num_heads=Hq, key_cache=key_cache, block_tables=block_tables, q_dtype=query.dtype,
+                     out_dtype=out_dtype)
+    num_groups = int(prefix_lens.shape[0])
+    nbytes = int(lib.paged_gqa_decode_shared_prefix_workspace_size(dims, num_groups, int(max_group_size),
+                                                                   int(max_seq_len), int(partition_size)))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
+    _call("paged_gqa_decode_shared_prefix",
+          lib.paged_gqa_decode_shared_prefix(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                             _ptr(block_tables), _ptr(seq_lens), _ptr(group_start),
+                                             _ptr(prefix_lens), num_groups, int(max_group_size), int(max_seq_len),
+                                             dims, float(scale), int(partition_size), _ptr(ws), wsb,
+                                             _stream(stream)))
     return out
 
 

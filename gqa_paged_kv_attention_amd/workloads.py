@@ -325,4 +325,32 @@ def cross_attention(seed: int = 6, num_seqs: int = 16, enc_lo: int = 1024, enc_h
                       query_lens=np.full(num_seqs, query_len, np.int32), dtype=BF16, rng=rng, cross=True, **kw)
 
 
+def shared_prefix_decode(seed: int = 7, num_groups: int = 4, group_size: int = 16, prefix_len: int = 2048,
+                         suffix_lo: int = 16, suffix_hi: int = 512, num_heads: int = 32, num_kv_heads: int = 8,
+                         head_dim: int = 128, block_size: int = 16, dtype: str = BF16, **kw):
+    """Decode batch of `num_groups` groups of `group_size` consecutive sequences.
+
+    The members of a group share their first `prefix_len` tokens: their block
+    tables point at the first member's pages for them (as with prefix caching;
+    `prefix_len` is a multiple of the page size), and each member then has
+    U{suffix_lo..suffix_hi} tokens of its own.  Returns (batch, group_start
+    [num_groups + 1], prefix_lens [num_groups]), both int32.
+    """
+    if prefix_len % block_size:
+        raise ValueError("prefix_len must be a multiple of block_size")
+    rng = np.random.default_rng(seed)
+    B = num_groups * group_size
+    suffix = rng.integers(suffix_lo, suffix_hi + 1, size=B)
+    bt = make_batch(name="shared_prefix_decode", seed=seed, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                    head_dim=head_dim, block_size=block_size, seq_lens=prefix_len + suffix,
+                    query_lens=np.ones(B, np.int32), dtype=dtype, rng=rng, **kw)
+    shared_pages = prefix_len // block_size
+    for g in range(num_groups):
+        first = g * group_size
+        bt.block_tables[first + 1:first + group_size, :shared_pages] = bt.block_tables[first, :shared_pages]
+    group_start = np.arange(0, B + 1, group_size, dtype=np.int32)
+    prefix_lens = np.full(num_groups, prefix_len, dtype=np.int32)
+    return bt, group_start, prefix_lens
+
+
 LONGCTX_PARTITION = 512

@@ -236,6 +236,47 @@ int32_t paged_cross_attention(void* out, const void* query, const void* key_cach
                               int32_t max_encoder_len, gqa_dims dims, float scale, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * paged_gqa_decode_shared_prefix: the decode of paged_gqa_decode for a batch
+ * whose sequences share prompt prefixes, reading each shared page once per
+ * group instead of once per sequence.  With automatic prefix caching the
+ * block tables of such sequences point at the same physical pages ("[Kernel]
+ * [V1] Further optimizations to ROCm (Triton) Backend to better handle GQA",
+ * benchmark discussion: prefix caching changes the measured results).
+ *
+ * Groups are ranges of consecutive sequences: group g is sequences
+ * [group_start[g], group_start[g + 1]) (group_start non-decreasing, within
+ * [0, num_seqs]); its members hold the same first prefix_lens[g] tokens, read
+ * through the block table of the group's first member.  Sequences in no group
+ * are decoded on their own.  The result is that of paged_gqa_decode on the
+ * same arguments (each sequence attends to its own seq_lens[b] tokens).
+ * Preconditions (device data, unchecked; a violation gives wrong rows, never
+ * an out-of-bounds access): prefix_lens[g] <= seq_lens of every member, group
+ * sizes <= max_group_size, seq_lens <= max_seq_len.
+ *
+ * bf16: the shared part of a group (its prefix rounded down to 64 keys) is
+ * attended by all members together: their query rows (member x head) form
+ * matrix-core tiles against each shared K/V tile, in chunks of 512 to 2048
+ * keys.  Each member's remaining keys run the decode in partitions of
+ * partition_size tokens (0: the library picks, at least 256).  The partials
+ * of both are merged by log-sum-exp.  The prefix tiles compute P.V on fp16
+ * matrix cores as chunked_prefill_paged_decode does (precondition
+ * |V| < 65504).  fp32: runs paged_gqa_decode (no sharing), with the same
+ * meaning of partition_size.
+ *
+ * Workspace (device, >= paged_gqa_decode_shared_prefix_workspace_size bytes
+ * for the same dims, num_groups, max_group_size, max_seq_len and
+ * partition_size; no initialisation needed): the partials and their counts.
+ */
+size_t paged_gqa_decode_shared_prefix_workspace_size(gqa_dims dims, int32_t num_groups, int32_t max_group_size,
+                                                    int32_t max_seq_len, int32_t partition_size);
+int32_t paged_gqa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* seq_lens, const int32_t* group_start,
+                                       const int32_t* prefix_lens, int32_t num_groups, int32_t max_group_size,
+                                       int32_t max_seq_len, gqa_dims dims, float scale, int32_t partition_size,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"reshape_and_cache", "paged_gqa_decode", "splitk_lse_reduce", "chunked_prefill_paged_decode",
             "paged_gqa_decode_workspace_size", "chunked_prefill_paged_decode_workspace_size",
             "paged_cross_attention", "paged_cross_attention_workspace_size",
+            "paged_gqa_decode_shared_prefix", "paged_gqa_decode_shared_prefix_workspace_size",
             "gqa_status_string", "gqa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -155,3 +156,29 @@ def test_cross_attention_validation(lib):
     n = lib.paged_cross_attention_workspace_size(d, 1000, 6400, 0)
     assert n == lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 6400, 0)
     assert cross(lib, d, num_tokens=1000, max_query_len=100, max_encoder_len=6400, ws=FAKE, wsb=n - 1) == WORKSPACE
+
+
+def shared(lib, d, num_groups=2, max_group_size=4, max_seq_len=4096, partition=0, ws=None, wsb=0, ptr=FAKE, gptr=FAKE):
+    return lib.paged_gqa_decode_shared_prefix(ptr, ptr, ptr, ptr, ptr, ptr, gptr, gptr, num_groups, max_group_size,
+                                              max_seq_len, d, 0.1, partition, ws, wsb, None)
+
+
+def test_shared_prefix_validation(lib):
+    d = dims()                                     # 4 sequences
+    n = lib.paged_gqa_decode_shared_prefix_workspace_size(d, 2, 4, 4096, 0)
+    # partials for at least 2 prefix chunks (of <= 2048 keys) + 1 suffix partition per (sequence, head)
+    assert n >= 4 * 32 * 3 * (128 + 1) * 4 and n % 256 == 0
+    # a fixed partition size sets the suffix slots: 4096 / 256 = 16 of them
+    assert lib.paged_gqa_decode_shared_prefix_workspace_size(d, 2, 4, 4096, 256) >= 4 * 32 * 17 * (128 + 1) * 4
+    assert shared(lib, d) == WORKSPACE
+    assert shared(lib, d, ws=FAKE, wsb=n - 1) == WORKSPACE
+    assert shared(lib, d, max_group_size=5) == INVALID          # larger than the batch
+    assert shared(lib, d, partition=48) == INVALID
+    assert shared(lib, d, num_groups=-1) == INVALID
+    assert shared(lib, d, gptr=None) == INVALID
+    assert shared(lib, d, ptr=None) == INVALID
+    assert shared(lib, dims(num_seqs=0), num_groups=0, max_group_size=0, ptr=None, gptr=None) == OK
+    assert lib.paged_gqa_decode_shared_prefix_workspace_size(d, 2, 5, 4096, 0) == 0
+    f32 = dims(q_dtype=ops.GQA_F32, kv_dtype=ops.GQA_F32)
+    assert lib.paged_gqa_decode_shared_prefix_workspace_size(f32, 2, 4, 4096, 512) == \
+        lib.paged_gqa_decode_workspace_size(f32, 4096, 512)
