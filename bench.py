@@ -40,7 +40,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "8ef5df7c17ec633043612a0102530c877b5957559d2783a5bf9146609bb66608", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645957480, "write_bytes_per_call": 6333802, "hbm_bytes_per_call": 652291282, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "e35bcf278e6a52afb6a02c2fc495b9dfe09d322f849c9d64f8aea8480bb3b4d2", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645985932, "write_bytes_per_call": 6333945, "hbm_bytes_per_call": 652319877, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
