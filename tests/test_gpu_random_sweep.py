@@ -1,0 +1,104 @@
+"""Seeded random configurations through every attention entry point, each
+compared with the CPU fp64 oracle at the usual bar (max-abs <= 1e-2 and
+relative L2 <= 2e-3 for bf16 inputs; fp32 inputs also relative L2 <= 1e-5).
+
+Each case draws the head shape, head size, page size, dtype, batch and
+lengths from its seed (all valid inputs), so the sweep reaches combinations
+the targeted tests do not list one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gqa_paged_kv_attention_amd import ops
+from gqa_paged_kv_attention_amd import workloads as wl
+from oracle import decode_ref, paged_attention_ref
+from tests.gpu_util import DeviceBatch, assert_parity, have_gpu, host, poison_tails
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+HEADS = [(4, 4), (8, 2), (8, 1), (12, 4), (16, 2), (24, 3), (32, 8), (32, 1), (40, 5), (64, 2)]
+
+
+def draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    return rng, dict(num_heads=hq, num_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
+                     block_size=int(rng.choice([16, 32, 64])),
+                     dtype=wl.F32 if rng.random() < 0.25 else wl.BF16)
+
+
+def lengths(rng, n, hi):
+    """Context lengths with some zeros, short and long ones."""
+    kind = rng.integers(3, size=n)
+    return np.where(kind == 0, rng.integers(0, 3, size=n),
+                    np.where(kind == 1, rng.integers(1, 64, size=n), rng.integers(64, hi, size=n)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode(seed):
+    rng, shape = draw(seed)
+    B = int(rng.integers(1, 24))
+    L = lengths(rng, B, 1500)
+    bt = wl.make_batch(name="rnd_dec", seed=seed, seq_lens=L, query_lens=np.minimum(L, 1), poison_slack=True,
+                       **shape)
+    bt.query = wl._normal_storage(rng, (B, shape["num_heads"], shape["head_dim"]), shape["dtype"])
+    poison_tails(bt)
+    partition = int(rng.choice([0, 32, 96, 256]))
+    got = host(DeviceBatch(bt).decode(partition))
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
+                     bt.scale)
+    assert_parity(got, ref, bt.dtype, f"{bt.describe()} P={partition}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("causal", [True, False])
+def test_random_mixed_and_cross(seed, causal):
+    rng, shape = draw(100 + seed)
+    B = int(rng.integers(1, 16))
+    L = lengths(rng, B, 900)
+    if causal:
+        q = np.where(rng.random(B) < 0.5, np.minimum(L, 1), rng.integers(0, L + 1))
+    else:
+        q = np.where(rng.random(B) < 0.4, 1, rng.integers(0, 200, size=B))
+    bt = wl.make_batch(name="rnd_mix", seed=seed, seq_lens=L, query_lens=q, poison_slack=True, cross=not causal,
+                       **shape)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    partition = int(rng.choice([0, 64, 512]))
+    got = host(dev.mixed(partition) if causal else dev.cross(partition))
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale, causal=causal)
+    assert_parity(got, ref, bt.dtype, f"{bt.describe()} causal={causal} P={partition}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shared_prefix(seed):
+    rng, shape = draw(200 + seed)
+    bs = shape["block_size"]
+    groups = []
+    for _ in range(int(rng.integers(1, 5))):
+        members = int(rng.integers(0, 12))
+        prefix = bs * int(rng.integers(0, 1200 // bs))
+        groups.append((members, prefix, [int(x) for x in rng.integers(0, 300, size=members)]))
+    seq_lens, starts, prefixes = [], [0], []
+    for members, prefix, suffixes in groups:
+        seq_lens += [prefix + s for s in suffixes]
+        starts.append(starts[-1] + members)
+        prefixes.append(prefix)
+    if not seq_lens:
+        pytest.skip("empty draw")
+    bt = wl.make_batch(name="rnd_sp", seed=seed, seq_lens=seq_lens, query_lens=[1] * len(seq_lens),
+                       poison_slack=True, **shape)
+    for g, (members, prefix, _) in enumerate(groups):
+        first = starts[g]
+        bt.block_tables[first + 1:first + members, :prefix // bs] = bt.block_tables[first, :prefix // bs]
+    dev = DeviceBatch(bt)
+    partition = int(rng.choice([0, 64, 256]))
+    got = host(ops.paged_gqa_decode_shared_prefix(
+        dev.query, dev.key_cache, dev.value_cache, dev.block_tables, dev.seq_lens,
+        ops.to_device(np.array(starts, np.int32)), ops.to_device(np.array(prefixes, np.int32)),
+        max(1, max(m for m, _, _ in groups)), bt.max_seq_len, bt.scale, partition_size=partition))
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
+                     bt.scale)
+    assert_parity(got, ref, bt.dtype, f"{bt.describe()} groups={[(m, p) for m, p, _ in groups]} P={partition}")
