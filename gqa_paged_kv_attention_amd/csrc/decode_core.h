@@ -342,7 +342,9 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   const int slot = uo ? uo->slot + p : p;
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int r = i / D, d = i % D;
-    const float v = sm_o[0][r][d] + sm_o[1][r][d] + sm_o[2][r][d] + sm_o[3][r][d];
+    float v = sm_o[0][r][d];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) v += sm_o[u][r][d];
     if (!partial)
       store1(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
     else

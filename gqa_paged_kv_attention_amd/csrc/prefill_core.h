@@ -42,7 +42,8 @@ struct PrefillLds {
   static constexpr int kBytes = 2 * (KBUF + VBUF) * 2;
   static constexpr int CH = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile, K and V each
   // chunk i of a thread comes from 16-token block i * PI + (thread / (kThreads / PI)) of the tile
-  static constexpr int PI = 128 / D;
+  static constexpr int PI = kThreads / (2 * D);
+  static_assert(PI == 1 || PI == 2 || PI == 4, "a copy chunk spans 1, 2 or 4 blocks");
 };
 
 // LDS banking (gfx950, measured): a 128-bit access is served 32 lanes at a
@@ -86,7 +87,10 @@ struct TileCopyPlan {
   template <class P>
   __device__ __forceinline__ P block_of(int i, const P* blocks) const {
     if (S::PI == 1) return blocks[i];
-    return pw ? blocks[i * S::PI + 1] : blocks[i * S::PI];
+    if (S::PI == 2) return pw ? blocks[i * S::PI + 1] : blocks[i * S::PI];
+    const P lo = (pw & 1) ? blocks[i * S::PI + 1] : blocks[i * S::PI];
+    const P hi = (pw & 1) ? blocks[i * S::PI + 3] : blocks[i * S::PI + 2];
+    return (pw & 2) ? hi : lo;
   }
 };
 
