@@ -40,7 +40,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "e35bcf278e6a52afb6a02c2fc495b9dfe09d322f849c9d64f8aea8480bb3b4d2", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645985932, "write_bytes_per_call": 6333945, "hbm_bytes_per_call": 652319877, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "0e6ff26772bc2a56d5a14a0c220271d834d5404da4aa8b22ac99ff37cf7c920a", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645982874, "write_bytes_per_call": 6332521, "hbm_bytes_per_call": 652315396, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():

@@ -179,8 +179,10 @@ __global__ __launch_bounds__(D) void stream_reduce_kernel(StreamArgs a) {
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const int w = wb + k;
-      // workers past the unit, or with an empty range (T < W), hold no segment
-      const bool has = w <= w1 && T * w / W != T * (w + 1) / W;
+      // workers past the unit, or with an empty range, hold no segment; every
+      // range holds at least floor(T / W) items, so only T < W needs the
+      // (64-bit, slow) division
+      const bool has = w <= w1 && (T >= W || T * w / W != T * (w + 1) / W);
       const size_t seg = ((size_t)w * 2 + (w == w0 ? slot0 : 0)) * G + g;
       lv[k] = has ? a.seg_lse[seg] : -INFINITY;
       ov[k] = has ? a.seg_out[seg * D + d] : 0.f;
