@@ -148,9 +148,26 @@ struct MergeCursor {
   }
 };
 
+// Position in the merged list of element r of one list, as MergeCursor gives
+// it, from the closed form: the quotient (2r + 1) n_other - n_self over
+// 2 n_self, in double precision.  It is exact: |numerator| < 2^41 and the
+// quotient < 2^21, so the rounding error (< 2^-32) cannot cross the distance
+// 1 / (2 n_self) >= 2^-21 to the next integer, and exact quotients are exact.
+__device__ __forceinline__ int merged_position(int r, int n_self, int n_other, bool decode) {
+  const double num = (2.0 * r + 1.0) * n_other - n_self;
+  const double qt = num / (2.0 * n_self);
+  long long before = decode ? (long long)floor(qt) + 1 : (long long)ceil(qt);
+  before = before < 0 ? 0 : (before > n_other ? n_other : before);
+  return r + (int)before;
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
   __shared__ int hist[2][kCostBuckets];      // [prefill, decode][cost bucket]
   __shared__ int wsum[kSchedThreads / 64];
+  // one sequence per thread (num_seqs <= kSchedThreads): flat start of its
+  // units, start in its list, unit count (negative: decode list), query range and length
+  __shared__ int s_flat[kSchedThreads], s_r0[kSchedThreads], s_nu[kSchedThreads];
+  __shared__ int s_info[kSchedThreads][3];
   for (int i = threadIdx.x; i < 2 * kCostBuckets; i += kSchedThreads) hist[i / kCostBuckets][i % kCostBuckets] = 0;
   __syncthreads();
   // the summary of this thread's first sequence is kept for the second pass
@@ -190,20 +207,59 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
-    int nu = nu0, cmax = cmax0;
-    bool dec = dec0;
-    SeqInfo info = info0;
-    if (b != threadIdx.x) dec = seq_summary(a, b, &nu, &cmax, &info);
-    if (!nu) continue;
-    // a contiguous range of its list; units heaviest first (the last row tile
-    // reaches furthest; decode partitions are in order)
-    MergeCursor cur(atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu), n_list[dec], n_list[!dec], dec);
-    for (int k = 0; k < nu; ++k, cur.next()) {
-      const int pos = cur.position();
+  if (a.num_seqs <= kSchedThreads) {
+    // One sequence per thread: each reserves its range, then all threads
+    // write the units together (a long chunk's units would otherwise be
+    // written one after another by its thread, which sets the kernel's end).
+    const int b = threadIdx.x;
+    int nu = 0, r0 = 0;
+    if (b < a.num_seqs && nu0) {
+      nu = nu0;
+      r0 = atomicAdd(&hist[dec0][unit_cost_bucket(cmax0)], nu0);
+    }
+    int total;
+    const int flat = block_exclusive_scan(nu, &total, wsum);
+    s_flat[b] = flat;
+    s_r0[b] = r0;
+    s_nu[b] = dec0 ? -nu : nu;
+    s_info[b][0] = info0.q0;
+    s_info[b][1] = info0.q1;
+    s_info[b][2] = info0.seq_len;
+    __syncthreads();
+    for (int f = threadIdx.x; f < total; f += kSchedThreads) {
+      // owner: the last sequence whose flat start is <= f (ranges are in
+      // sequence order; an empty sequence shares its successor's start, so
+      // the last such sequence is never empty)
+      int lo = 0, hi = kSchedThreads;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_flat[mid] <= f) lo = mid; else hi = mid;
+      }
+      const bool dec = s_nu[lo] < 0;
+      const int n = dec ? -s_nu[lo] : s_nu[lo];
+      const int k = f - s_flat[lo];
+      const int pos = merged_position(s_r0[lo] + k, n_list[dec], n_list[!dec], dec);
       if (pos < a.unit_capacity) {
-        a.units[pos].a = make_int4(b, dec ? -1 - k : nu - 1 - k, info.q0, info.q1);
-        a.units[pos].b = make_int4(info.seq_len, 0, 0, 0);
+        a.units[pos].a = make_int4(lo, dec ? -1 - k : n - 1 - k, s_info[lo][0], s_info[lo][1]);
+        a.units[pos].b = make_int4(s_info[lo][2], 0, 0, 0);
+      }
+    }
+  } else {
+    for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
+      int nu = nu0, cmax = cmax0;
+      bool dec = dec0;
+      SeqInfo info = info0;
+      if (b != threadIdx.x) dec = seq_summary(a, b, &nu, &cmax, &info);
+      if (!nu) continue;
+      // a contiguous range of its list; units heaviest first (the last row tile
+      // reaches furthest; decode partitions are in order)
+      MergeCursor cur(atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu), n_list[dec], n_list[!dec], dec);
+      for (int k = 0; k < nu; ++k, cur.next()) {
+        const int pos = cur.position();
+        if (pos < a.unit_capacity) {
+          a.units[pos].a = make_int4(b, dec ? -1 - k : nu - 1 - k, info.q0, info.q1);
+          a.units[pos].b = make_int4(info.seq_len, 0, 0, 0);
+        }
       }
     }
   }

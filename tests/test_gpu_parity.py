@@ -275,6 +275,22 @@ def test_mixed_long_decodes_split_by_library(dtype):
     assert_parity(host(dev.mixed(0)), ref, dtype, bt.describe())
 
 
+def test_mixed_more_sequences_than_schedule_threads():
+    """Over 1024 sequences the scheduling pass lets each thread write several
+    sequences' units (below that, all threads write the units together)."""
+    rng = np.random.default_rng(71)
+    B = 1100
+    q_lens = np.where(rng.random(B) < 0.85, 1, rng.integers(2, 24, size=B))
+    seq_lens = q_lens + rng.integers(0, 90, size=B)
+    bt = wl.make_batch(name="many", seed=72, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                       seq_lens=seq_lens, query_lens=q_lens, dtype=wl.BF16)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale)
+    dev = DeviceBatch(bt)
+    for partition in (0, 32):
+        assert_parity(host(dev.mixed(partition)), ref, bt.dtype, f"{bt.describe()} P={partition}")
+
+
 def test_mixed_bf16_output_is_rounded_fp32():
     """bf16 output of the mixed call is the fp32 result rounded to bf16."""
     bt = wl.mixed_chunked(seed=4, num_seqs=24, token_budget=900)
