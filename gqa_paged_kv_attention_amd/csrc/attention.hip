@@ -13,7 +13,7 @@ namespace {
 template <class Tile, int D, int NT, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void decode_kernel(DecodeArgs a) {
-  __shared__ float lds[DecodeMergeLds<D, NT>::kFloats];
+  __shared__ __attribute__((aligned(16))) float lds[DecodeMergeLds<D, NT>::kFloats];
   decode_partition<Tile, D, NT, OutT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 

@@ -281,8 +281,8 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
 
   if (nparts == 0) {
     if (p == 0 && !uo)
-      for (int i = threadIdx.x; i < G * D; i += kThreads)
-        store1(out + ((size_t)row * a.num_heads + kv * G) * D + i, 0.f);
+      for (int i = threadIdx.x; i < G * D / 4; i += kThreads)
+        store4(out + ((size_t)row * a.num_heads + kv * G) * D + 4 * i, zero4());
     return;
   }
   if (p >= nparts) return;
@@ -340,15 +340,17 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   float* part_lse = uo ? uo->part_lse : a.partial_lse;
   const int stride = uo ? uo->slots : a.max_partitions;
   const int slot = uo ? uo->slot + p : p;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int r = i / D, d = i % D;
-    float v = sm_o[0][r][d];
+  // four channels per thread: 16-byte LDS reads (rows of D + 4 floats stay
+  // 16-byte aligned), 16-byte fp32 or 8-byte bf16 stores
+  for (int i = threadIdx.x; i < G * D / 4; i += kThreads) {
+    const int r = 4 * i / D, d = 4 * i % D;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sm_o[0][r][d]);
 #pragma unroll
-    for (int u = 1; u < kWaves; ++u) v += sm_o[u][r][d];
+    for (int u = 1; u < kWaves; ++u) v += *reinterpret_cast<const f32x4_t*>(&sm_o[u][r][d]);
     if (!partial)
-      store1(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
+      store4(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
     else
-      part_out[((head0 + r) * stride + slot) * D + d] = v;
+      store4(part_out + ((head0 + r) * stride + slot) * D + d, v);
   }
   if (partial && threadIdx.x < G) {
     const int r = threadIdx.x;

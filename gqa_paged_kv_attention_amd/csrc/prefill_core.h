@@ -358,15 +358,17 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   for (int it = t_begin; it < n_tiles; ++it) {
     const int buf = (it - t_begin) & 1;
     const int tb = it * kKeyTile;
-    // tile it + 1 (loaded during the previous iteration) -> the other buffer,
-    // which every wave finished reading before the last barrier; then the
-    // loads of tile it + 2, and the block-table entries of tile it + 3
+    // tile it from its buffer; then tile it + 1 (loaded during the previous
+    // iteration) -> the other buffer, which every wave finished reading
+    // before the last barrier; then the loads of tile it + 2 and the block-
+    // table entries of tile it + 3.  Computing first lets the first tile of
+    // a unit start while the second is still arriving.
+    if (tb <= lim_hi) compute(sK + buf * S::KBUF, sV + buf * S::VBUF, tb, tb + kKeyTile - 1 > lim_lo);
     if (it + 1 < n_tiles)
       store_tile_lds<D, NTW, BS>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan, tb + kKeyTile, L,
                              tb + 2 * kKeyTile > L);
     if (it + 2 < n_tiles) issue(raw, kreg, vreg);
     fetch_pages(it + 3, raw);
-    if (tb <= lim_hi) compute(sK + buf * S::KBUF, sV + buf * S::VBUF, tb, tb + kKeyTile - 1 > lim_lo);
     __syncthreads();
   }
 
