@@ -363,6 +363,61 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   }
 }
 
+// Partition p of (sequence b, kv head kv) run by this wave alone, for query
+// row `row` and seq_lens[b] = seq_len: the same split into partitions as
+// decode_partition_at, its tiles walked in pairs by the wave's own pipeline,
+// and no merge between waves.  It writes `out` when the sequence has one
+// partition, else the partition's normalised partial and log-sum-exp.
+template <class Tile, int D, int NT, class OutT>
+__device__ __forceinline__ void decode_wave_partition(const DecodeArgs& a, int p, int kv, int b, int row,
+                                                      int seq_len) {
+  const int G = a.group;
+  const int lane = lane_id();
+  const int n = lane & 15, q = lane >> 4;
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  const int L = min(clamp_len(seq_len, a.max_blocks_per_seq, Tile::kBS), a.max_partitions * a.partition_size);
+  const int nparts = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 0;
+  if (nparts == 0) {
+    if (p == 0)
+      for (int i = lane; i < G * D / 4; i += kWave)
+        store4(out + ((size_t)row * a.num_heads + kv * G) * D + 4 * i, zero4());
+    return;
+  }
+  if (p >= nparts) return;
+  const int tiles_all = (L + kTile - 1) / kTile;
+  const int per = tiles_all / nparts, extra = tiles_all % nparts;
+  const int tile0 = p * per + min(p, extra);
+  const int n_tiles = per + (p < extra ? 1 : 0);
+  const int t1 = min((tile0 + n_tiles) * kTile, L);
+
+  typename Tile::Q qf[NT];
+  load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
+  WaveState<Tile, NT> st;
+  st.reset();
+  run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
+                         a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0, tile0 + n_tiles, 1, a.scale_log2, lane);
+
+  const size_t head0 = (size_t)b * a.num_heads + kv * G;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int g = nt * 16 + n;
+    const float lr = row_sum4(st.l[nt]);
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    if (g >= G) continue;
+    if (nparts == 1) {
+      OutT* dst = out + ((size_t)row * a.num_heads + kv * G + g) * D + 4 * q;
+#pragma unroll
+      for (int dt = 0; dt < Tile::DT; ++dt) store4(dst + dt * 16, st.o[nt][dt] * inv);
+    } else {
+      float* dst = a.partial_out + ((head0 + g) * a.max_partitions + p) * D + 4 * q;
+#pragma unroll
+      for (int dt = 0; dt < Tile::DT; ++dt) store4(dst + dt * 16, st.o[nt][dt] * inv);
+      if (q == 0)
+        a.partial_lse[(head0 + g) * a.max_partitions + p] = lr > 0.f ? (st.m[nt] + __log2f(lr)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // As decode_partition_at, reading the query row (sequence b's only new token
 // when query_start_loc is given, else row b) and seq_lens[b] itself.
 template <class Tile, int D, int NT, class OutT>

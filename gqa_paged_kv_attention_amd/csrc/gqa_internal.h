@@ -123,13 +123,23 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bo
 // decreasing cost; the fused kernel runs unit i / Hkv for kv head i % Hkv.
 // Rows of a prefill unit (depends only on the build):
 int prefill_lds_rows_per_group();
-// A scheduled unit: sequence b, code (>= 0: prefill row tile; < 0: decode
-// partition -1 - code), the sequence's query_start_loc[b], [b + 1] and
-// seq_lens[b], so that the unit's work-group reads them with the unit.
+// A scheduled unit, four 16-byte slots, read by its work-group together with
+// the unit count.
+//  - Prefill row tile rt of sequence b: s[0] = {b, rt, q0, q1} (the sequence's
+//    query_start_loc[b], [b + 1]), s[1] = {seq_len, 0, 0, 0}.
+//  - Decode partition p of sequence b run by the whole work-group (a long
+//    partition): s[0] = {b, -1 - p, row, seq_len} (row: the sequence's query
+//    row), s[1].x = kUnitWholeGroup.
+//  - Up to four short decode partitions, one per wave: s[w] = {b, -1 - p, row,
+//    seq_len} for wave w, s[w].x = kUnitEmpty for a wave without one.
 struct MixedUnit {
-  int4 a;                           // {b, code, q0, q1}
-  int4 b;                           // {seq_len, 0, 0, 0}
+  int4 s[4];
 };
+constexpr int kUnitEmpty = -1;
+constexpr int kUnitWholeGroup = -2;
+// Decode partitions of more 32-token tiles than this are run by a whole
+// work-group (its waves take the tiles round-robin); shorter ones by one wave.
+constexpr int kWaveDecodeMaxTiles = 32;
 struct ScheduleArgs {
   const int32_t* seq_lens;
   const int32_t* query_start_loc;

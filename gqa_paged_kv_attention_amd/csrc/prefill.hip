@@ -69,7 +69,7 @@ __device__ __forceinline__ bool seq_summary(const ScheduleArgs& a, int b, int* u
     const int tiles_all = (Lp + kTile - 1) / kTile;
     const int first = tiles_all / nparts + (tiles_all % nparts ? 1 : 0);
     *units = nparts;
-    *cost = (first + 3) / 4;
+    *cost = first;
     return true;
   }
   const int prior = L - q_len;
@@ -161,6 +161,41 @@ __device__ __forceinline__ int merged_position(int r, int n_self, int n_other, b
   return r + (int)before;
 }
 
+// Sizes of the two lists of the merged order.  Prefill row tiles are one unit
+// each.  Decode partitions are listed costliest first: the n_long partitions of
+// more than kWaveDecodeMaxTiles tiles are one (whole work-group) unit each; the
+// rest are packed four to a unit, one per wave, so that neighbours in a pack
+// have similar lengths.
+struct ListSizes {
+  int n_pf, n_dec, n_long, n_du;
+};
+
+__device__ __forceinline__ void write_prefill_unit(const ScheduleArgs& a, int pos, int b, int rt, const SeqInfo& in) {
+  if (pos >= a.unit_capacity) return;
+  a.units[pos].s[0] = make_int4(b, rt, in.q0, in.q1);
+  a.units[pos].s[1] = make_int4(in.seq_len, 0, 0, 0);
+}
+
+// Decode partition k of sequence b, element r of the decode list.
+__device__ __forceinline__ void write_decode_element(const ScheduleArgs& a, const ListSizes& z, int r, int b, int k,
+                                                     const SeqInfo& in) {
+  const int4 e = make_int4(b, -1 - k, in.q0, in.seq_len);
+  if (r < z.n_long) {
+    const int pos = merged_position(r, z.n_du, z.n_pf, true);
+    if (pos >= a.unit_capacity) return;
+    a.units[pos].s[0] = e;
+    a.units[pos].s[1] = make_int4(kUnitWholeGroup, 0, 0, 0);
+    return;
+  }
+  const int sr = r - z.n_long, pack = sr / 4, w = sr % 4;
+  const int pos = merged_position(z.n_long + pack, z.n_du, z.n_pf, true);
+  if (pos >= a.unit_capacity) return;
+  a.units[pos].s[w] = e;
+  if (w == 0)
+    for (int j = min(4, z.n_dec - z.n_long - 4 * pack); j < 4; ++j)
+      a.units[pos].s[j] = make_int4(kUnitEmpty, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
   __shared__ int hist[2][kCostBuckets];      // [prefill, decode][cost bucket]
   __shared__ int wsum[kSchedThreads / 64];
@@ -207,6 +242,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     }
   }
   __syncthreads();
+  // decode partitions costlier than kWaveDecodeMaxTiles tiles: the start of its bucket
+  ListSizes z;
+  z.n_pf = n_list[0];
+  z.n_dec = n_list[1];
+  z.n_long = hist[1][unit_cost_bucket(kWaveDecodeMaxTiles)];
+  z.n_du = z.n_long + (z.n_dec - z.n_long + 3) / 4;
+  __syncthreads();
   if (a.num_seqs <= kSchedThreads) {
     // One sequence per thread: each reserves its range, then all threads
     // write the units together (a long chunk's units would otherwise be
@@ -238,11 +280,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
       const bool dec = s_nu[lo] < 0;
       const int n = dec ? -s_nu[lo] : s_nu[lo];
       const int k = f - s_flat[lo];
-      const int pos = merged_position(s_r0[lo] + k, n_list[dec], n_list[!dec], dec);
-      if (pos < a.unit_capacity) {
-        a.units[pos].a = make_int4(lo, dec ? -1 - k : n - 1 - k, s_info[lo][0], s_info[lo][1]);
-        a.units[pos].b = make_int4(s_info[lo][2], 0, 0, 0);
-      }
+      const SeqInfo in{s_info[lo][0], s_info[lo][1], s_info[lo][2]};
+      if (dec)
+        write_decode_element(a, z, s_r0[lo] + k, lo, k, in);
+      else
+        write_prefill_unit(a, merged_position(s_r0[lo] + k, z.n_pf, z.n_du, false), lo, n - 1 - k, in);
     }
   } else {
     for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
@@ -253,17 +295,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
       if (!nu) continue;
       // a contiguous range of its list; units heaviest first (the last row tile
       // reaches furthest; decode partitions are in order)
-      MergeCursor cur(atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu), n_list[dec], n_list[!dec], dec);
-      for (int k = 0; k < nu; ++k, cur.next()) {
-        const int pos = cur.position();
-        if (pos < a.unit_capacity) {
-          a.units[pos].a = make_int4(b, dec ? -1 - k : nu - 1 - k, info.q0, info.q1);
-          a.units[pos].b = make_int4(info.seq_len, 0, 0, 0);
-        }
+      const int r0 = atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu);
+      if (dec) {
+        for (int k = 0; k < nu; ++k) write_decode_element(a, z, r0 + k, b, k, info);
+      } else {
+        MergeCursor cur(r0, z.n_pf, z.n_du, false);
+        for (int k = 0; k < nu; ++k, cur.next()) write_prefill_unit(a, cur.position(), b, nu - 1 - k, info);
       }
     }
   }
-  if (threadIdx.x == 0) *a.unit_count = min(n_list[0] + n_list[1], a.unit_capacity);
+  if (threadIdx.x == 0) *a.unit_count = min(z.n_pf + z.n_du, a.unit_capacity);
 }
 
 // ---------------------------------------------------------------------------
@@ -283,15 +324,20 @@ void mixed_kernel(MixedArgs a) {
   const int slot = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
   // the record is read together with the count (slot < the list's capacity)
   const int count = *a.unit_count;
-  const int4 u = a.units[slot].a;
-  const int seq_len = a.units[slot].b.x;
+  const int4 u = a.units[slot].s[0];
+  const int4 u1 = a.units[slot].s[1];
   if (slot >= count) return;
   if (u.y >= 0) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, seq_len, kv, sK, sK + 2 * S::KBUF);
-  } else {
-    decode_partition_at<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, seq_len,
+    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, u1.x, kv, sK, sK + 2 * S::KBUF);
+  } else if (u1.x == kUnitWholeGroup) {
+    decode_partition_at<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, u.w,
                                                       reinterpret_cast<float*>(lds));
+  } else {
+    // one short decode partition per wave (the branch is uniform per wave)
+    const int w = wave_id();
+    const int4 e = a.units[slot].s[w];
+    if (e.x >= 0) decode_wave_partition<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - e.y, kv, e.x, e.z, e.w);
   }
 }
 
