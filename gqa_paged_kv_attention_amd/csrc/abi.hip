@@ -279,6 +279,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
 
     gqa::ScheduleArgs sa;
     sa.seq_lens = seq_lens;
+    sa.block_tables = block_tables;
     sa.query_start_loc = query_start_loc;
     sa.units = units;
     sa.unit_count = count;

@@ -126,7 +126,10 @@ int prefill_lds_rows_per_group();
 // A scheduled unit, four 16-byte slots, read by its work-group together with
 // the unit count.
 //  - Prefill row tile rt of sequence b: s[0] = {b, rt, q0, q1} (the sequence's
-//    query_start_loc[b], [b + 1]), s[1] = {seq_len, 0, 0, 0}.
+//    query_start_loc[b], [b + 1]), s[1] = {seq_len, 0, 0, 0}, s[2], s[3] =
+//    block_tables[b][min(j, pages - 1)] for j = 0..7: the pages of the first
+//    two 64-key tiles, so that the unit's first K/V loads wait on no other
+//    load than the record's.
 //  - Decode partition p of sequence b run by the whole work-group (a long
 //    partition): s[0] = {b, -1 - p, row, seq_len} (row: the sequence's query
 //    row), s[1].x = kUnitWholeGroup.
@@ -142,6 +145,7 @@ constexpr int kUnitWholeGroup = -2;
 constexpr int kWaveDecodeMaxTiles = 32;
 struct ScheduleArgs {
   const int32_t* seq_lens;
+  const int32_t* block_tables;
   const int32_t* query_start_loc;
   MixedUnit* units;                 // [unit_capacity]
   int* unit_count;

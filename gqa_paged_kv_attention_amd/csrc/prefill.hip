@@ -172,8 +172,16 @@ struct ListSizes {
 
 __device__ __forceinline__ void write_prefill_unit(const ScheduleArgs& a, int pos, int b, int rt, const SeqInfo& in) {
   if (pos >= a.unit_capacity) return;
+  const int L = clamp_len(in.seq_len, a.max_blocks_per_seq, a.block_size);
+  const int last = max((L + a.block_size - 1) / a.block_size - 1, 0);
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  int e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = bt[min(j, last)];
   a.units[pos].s[0] = make_int4(b, rt, in.q0, in.q1);
   a.units[pos].s[1] = make_int4(in.seq_len, 0, 0, 0);
+  a.units[pos].s[2] = make_int4(e[0], e[1], e[2], e[3]);
+  a.units[pos].s[3] = make_int4(e[4], e[5], e[6], e[7]);
 }
 
 // Decode partition k of sequence b, element r of the decode list.
@@ -329,7 +337,10 @@ void mixed_kernel(MixedArgs a) {
   if (slot >= count) return;
   if (u.y >= 0) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, u1.x, kv, sK, sK + 2 * S::KBUF);
+    const int4 p0 = a.units[slot].s[2], p1 = a.units[slot].s[3];
+    const int first_pages[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, u1.x, kv, sK, sK + 2 * S::KBUF, 0, UnitOut(),
+                                       first_pages);
   } else if (u1.x == kUnitWholeGroup) {
     decode_partition_at<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, u.w,
                                                       reinterpret_cast<float*>(lds));

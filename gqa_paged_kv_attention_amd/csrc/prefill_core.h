@@ -150,11 +150,13 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 // otherwise (cross-attention) every row sees all seq_len keys, and q_len may
 // exceed seq_len.  Keys before 64 * t_begin are skipped (a split over keys).
 // Pages hold BS tokens.  sK / sV: two LDS buffers of KBUF and VBUF elements
-// each.
+// each.  `first_pages`, when given (t_begin = 0 only), holds
+// block_tables[b][min(j, pages - 1)] for j = 0..7, the entries of tiles 0 and
+// 1, already loaded with the unit.
 template <int D, int NTW, int BS, class OutT>
 __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int q0, int q1, int seq_len, int kv,
                                              uint16_t* sK, uint16_t* sV, int t_begin = 0,
-                                             const UnitOut& uo = UnitOut()) {
+                                             const UnitOut& uo = UnitOut(), const int* first_pages = nullptr) {
   typedef PrefillLds<D, NTW> S;
   const int G = a.group;
   const int q_len = q1 - q0;
@@ -254,9 +256,17 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   uint4 kreg[S::CH], vreg[S::CH];
   int raw[kEntries];
   if (n_tiles > t_begin) {               // uniform over the work-group
-    fetch_pages(t_begin, raw);
-    issue(raw, kreg, vreg);
-    fetch_pages(t_begin + 1, raw);
+    if (first_pages) {
+      // tile 0's entries and, when there is a tile 1, its entries (the same
+      // values fetch_pages(1) reads)
+      issue(first_pages, kreg, vreg);
+#pragma unroll
+      for (int j = 0; j < kEntries; ++j) raw[j] = first_pages[kEntries + j];
+    } else {
+      fetch_pages(t_begin, raw);
+      issue(raw, kreg, vreg);
+      fetch_pages(t_begin + 1, raw);
+    }
     store_tile_lds<D, NTW, BS>(sK, sV, kreg, vreg, plan, t_begin * kKeyTile, L, (t_begin + 1) * kKeyTile > L);
     if (n_tiles > t_begin + 1) issue(raw, kreg, vreg);
     fetch_pages(t_begin + 2, raw);
