@@ -46,7 +46,7 @@ template <class Tile, int D, int NT, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void stream_decode_kernel(StreamArgs a) {
   extern __shared__ int s_pref[];          // [B + 1] exclusive prefix of tiles * Hkv
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_scan[kWaves];
   const int B = a.num_seqs, G = a.group;
   const int lane = lane_id();
   const int n = lane & 15, q = lane >> 4;
@@ -67,16 +67,22 @@ void stream_decode_kernel(StreamArgs a) {
         for (int i = 0; i < a.num_heads * D; ++i) store1(out + (size_t)row * a.num_heads * D + i, 0.f);
       }
     }
-    s_scan[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = (threadIdx.x >= off) ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += add;
-      __syncthreads();
+    // inclusive scan within the wave (lane shuffles), then across the four
+    // wave totals: two barriers per chunk
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
     }
-    if (b < B) s_pref[b + 1] = running + s_scan[threadIdx.x];
-    running += s_scan[kThreads - 1];
+    const int w = wave_id();
+    if (lane == kWave - 1) s_scan[w] = x;
+    __syncthreads();
+    int base = running;
+    for (int i = 0; i < w; ++i) base += s_scan[i];
+    if (b < B) s_pref[b + 1] = base + x;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) running += s_scan[i];
     __syncthreads();
   }
   if (threadIdx.x == 0) s_pref[0] = 0;
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int kv = blockIdx.x % a.num_kv_heads;
   const int tile = blockIdx.x / a.num_kv_heads;
 
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_scan[kThreads];          // one entry per thread: locate_prefill_tile scans over them
   __shared__ int s_found[2];
   int local = 0;
   const int b = locate_prefill_tile(a.query_start_loc, a.num_seqs, G, RWG, tile, s_scan, s_found, &local);
