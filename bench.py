@@ -11,8 +11,8 @@ Also reported: the decode kernel's roofline (HIP events on its launch
 stream), the mixed chunked-prefill + decode batch's tokens/s, the GQA saving
 against the same cache expanded per query head, cross-attention over a static
 encoder cache, the decode per page size, the shared-prefix decode against the
-plain decode, and the CPU oracle's throughput on a bounded sample as a
-baseline.
+plain decode, the 16 x 32k-token split-K decode, and the CPU oracle's
+throughput on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
        python bench.py --copy-calibration   (a plain 512 MiB device copy, for
@@ -40,7 +40,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "69169e11cc2044ae096cbc91751685373ce18e829b72d653f4629462cd7c101f", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645882735, "write_bytes_per_call": 6333164, "hbm_bytes_per_call": 652215899, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "996decda1c96876765a7996d8fe7b08379f0812e0461f0cad713ad483d5f6723", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645914871, "write_bytes_per_call": 6333030, "hbm_bytes_per_call": 652247901, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention leg")
     ap.add_argument("--no-page-sizes", action="store_true", help="skip the 16/32/64-token page comparison")
     ap.add_argument("--no-shared-prefix", action="store_true", help="skip the shared-prefix decode comparison")
+    ap.add_argument("--no-long-context", action="store_true", help="skip the 16 x 32k-token split-K decode")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -214,6 +215,38 @@ def cross_attention_leg(dev, stream, reps):
                                      "tokens_per_s": round(bt.num_tokens / (ms * 1e-3), 1),
                                      "mfma_util": round(flops / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
         del q, kc, vc, out, ws
+    return res
+
+
+def long_context_leg(dev, stream, reps):
+    """Long-context split-K decode: 16 sequences of 32768 tokens, Hq=64, Hkv=8,
+    d=128, bf16 (2.15 GB of K+V), with 512-token partitions merged by
+    log-sum-exp (splitk_lse_reduce inside the call) and with the split the
+    library picks (balanced workers + merge)."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    bt = wl.longctx_splitk(seed=5)
+    up = lambda a: ops.to_device(a, dev)
+    q, kc, vc, tb, sl = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.block_tables), up(bt.seq_lens)
+    out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+    dims = ops.make_dims(num_seqs=bt.num_seqs, num_heads=bt.num_heads, key_cache=kc, block_tables=tb,
+                         q_dtype=q.dtype, out_dtype=out.dtype)
+    res = {"workload": "longctx_splitk (16 seqs x 32768 tokens, Hq=64, Hkv=8, d=128, bf16)",
+           "kv_bytes": bt.kv_bytes()}
+    for part in (512, 0):
+        ws = torch.zeros(max(ops.decode_workspace_size(dims, bt.max_seq_len, part), 1), dtype=torch.uint8,
+                         device=dev)
+        f = lambda: ops.paged_gqa_decode(q, kc, vc, tb, sl, bt.max_seq_len, bt.scale, partition_size=part, out=out,
+                                         workspace=ws)
+        warm_up(f, stream)
+        ms = event_time_ms(f, reps, stream)
+        gbs = bt.kv_bytes() / (ms * 1e-3) / 1e9
+        res["partition_512" if part else "library_split"] = {"us": round(ms * 1e3, 2), "kv_gbs": round(gbs, 1),
+                                                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del ws
+    del q, kc, vc, out
     return res
 
 
@@ -419,6 +452,9 @@ def main():
 
     if not args.no_shared_prefix:
         record["shared_prefix"] = shared_prefix_leg(dev, stream, 30)
+
+    if not args.no_long_context:
+        record["long_context"] = long_context_leg(dev, stream, 20)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)
