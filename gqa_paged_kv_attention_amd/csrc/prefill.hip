@@ -170,14 +170,19 @@ struct ListSizes {
   int n_pf, n_dec, n_long, n_du;
 };
 
-__device__ __forceinline__ void write_prefill_unit(const ScheduleArgs& a, int pos, int b, int rt, const SeqInfo& in) {
-  if (pos >= a.unit_capacity) return;
-  const int L = clamp_len(in.seq_len, a.max_blocks_per_seq, a.block_size);
+// block_tables[b][min(j, pages - 1)] for j = 0..7: the pages of a prefill
+// unit's first two 64-key tiles.
+__device__ __forceinline__ void first_pages(const ScheduleArgs& a, int b, int seq_len, int e[8]) {
+  const int L = clamp_len(seq_len, a.max_blocks_per_seq, a.block_size);
   const int last = max((L + a.block_size - 1) / a.block_size - 1, 0);
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  int e[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) e[j] = bt[min(j, last)];
+}
+
+__device__ __forceinline__ void write_prefill_unit(const ScheduleArgs& a, int pos, int b, int rt, const SeqInfo& in,
+                                                   const int e[8]) {
+  if (pos >= a.unit_capacity) return;
   a.units[pos].s[0] = make_int4(b, rt, in.q0, in.q1);
   a.units[pos].s[1] = make_int4(in.seq_len, 0, 0, 0);
   a.units[pos].s[2] = make_int4(e[0], e[1], e[2], e[3]);
@@ -211,12 +216,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   // units, start in its list, unit count (negative: decode list), query range and length
   __shared__ int s_flat[kSchedThreads], s_r0[kSchedThreads], s_nu[kSchedThreads];
   __shared__ int s_info[kSchedThreads][3];
+  __shared__ int s_pages[kSchedThreads][8];   // first_pages() of a prefill sequence
   for (int i = threadIdx.x; i < 2 * kCostBuckets; i += kSchedThreads) hist[i / kCostBuckets][i % kCostBuckets] = 0;
   __syncthreads();
   // the summary of this thread's first sequence is kept for the second pass
   int nu0 = 0, cmax0 = 0;
   bool dec0 = false;
   SeqInfo info0{0, 0, 0};
+  int pages0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
     int nu, cmax;
     SeqInfo info;
@@ -226,6 +233,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
       cmax0 = cmax;
       dec0 = dec;
       info0 = info;
+      // loaded now, so that the loads overlap the scans below
+      if (nu && !dec) first_pages(a, b, info.seq_len, pages0);
     }
     if (nu) atomicAdd(&hist[dec][unit_cost_bucket(cmax)], nu);
   }
@@ -275,6 +284,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     s_info[b][0] = info0.q0;
     s_info[b][1] = info0.q1;
     s_info[b][2] = info0.seq_len;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_pages[b][j] = pages0[j];
     __syncthreads();
     for (int f = threadIdx.x; f < total; f += kSchedThreads) {
       // owner: the last sequence whose flat start is <= f (ranges are in
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
       if (dec)
         write_decode_element(a, z, s_r0[lo] + k, lo, k, in);
       else
-        write_prefill_unit(a, merged_position(s_r0[lo] + k, z.n_pf, z.n_du, false), lo, n - 1 - k, in);
+        write_prefill_unit(a, merged_position(s_r0[lo] + k, z.n_pf, z.n_du, false), lo, n - 1 - k, in, s_pages[lo]);
     }
   } else {
     for (int b = threadIdx.x; b < a.num_seqs; b += kSchedThreads) {
@@ -307,8 +318,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
       if (dec) {
         for (int k = 0; k < nu; ++k) write_decode_element(a, z, r0 + k, b, k, info);
       } else {
+        int e[8];
+        first_pages(a, b, info.seq_len, e);
         MergeCursor cur(r0, z.n_pf, z.n_du, false);
-        for (int k = 0; k < nu; ++k, cur.next()) write_prefill_unit(a, cur.position(), b, nu - 1 - k, info);
+        for (int k = 0; k < nu; ++k, cur.next()) write_prefill_unit(a, cur.position(), b, nu - 1 - k, info, e);
       }
     }
   }

@@ -275,6 +275,30 @@ def test_mixed_long_decodes_split_by_library(dtype):
     assert_parity(host(dev.mixed(0)), ref, dtype, bt.describe())
 
 
+@pytest.mark.parametrize("n_short", [1, 2, 3, 4, 5, 9])
+def test_mixed_decode_packs(n_short):
+    """Decode partitions of at most 32 tiles run one per wave, four to a
+    work-group; longer ones run on a whole work-group.  n_short short decodes
+    leave the last pack with 1..4 partitions; lengths at the 32-tile boundary
+    (1024 keys: packed; 1025: whole work-group) and empty and one-key decodes
+    sit beside prefill chunks."""
+    rng = np.random.default_rng(90 + n_short)
+    short = list(rng.integers(1, 1025, size=n_short))
+    short[0] = 1024
+    q_lens = [1] * n_short + [1, 1, 1, 40, 3]
+    seq_lens = short + [1025, 1, 2900, 300, 45]
+    q_lens.append(0)
+    seq_lens.append(5)
+    bt = wl.make_batch(name="packs", seed=91 + n_short, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       seq_lens=seq_lens, query_lens=q_lens, dtype=wl.BF16, poison_slack=True)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale)
+    for partition in (0, 512):
+        assert_parity(host(dev.mixed(partition)), ref, bt.dtype, f"{bt.describe()} P={partition}")
+
+
 def test_mixed_more_sequences_than_schedule_threads():
     """Over 1024 sequences the scheduling pass lets each thread write several
     sequences' units (below that, all threads write the units together)."""
