@@ -1,8 +1,10 @@
 """Benchmark: paged GQA decode on Llama-3.1-8B shapes (one MI355X).
 
 One step = the whole decode hot path on one batch: write the step's new K/V
-into the paged cache (reshape_and_cache), then paged GQA attention with
-split-K partitions merged by log-sum-exp (paged_gqa_decode).  Workload: 64
+into the paged cache and run paged GQA attention with split-K partitions
+merged by log-sum-exp, as one call (paged_gqa_decode_append: the cache write
+fused into the balanced decode kernel).  The same step as two calls
+(reshape_and_cache, then paged_gqa_decode) is reported beside it.  Workload: 64
 sequences, Hq=32, Hkv=8, d=128, block 16, bf16 cache, context U{512..4096},
 randomly permuted pages, seeded synthetic N(0,1) data.
 
@@ -33,10 +35,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 
-# HBM traffic of one paged_gqa_decode call on this workload (both of its
-# kernels), from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB
+# HBM traffic of one step call (paged_gqa_decode_append on this workload, both
+# of its kernels), from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB
 # per dispatch) over `bench.py --steps 20 --warmup 5 --no-mixed
-# --no-cpu-baseline`, each scaled by what the same counter reads for the
+# --no-cpu-baseline --no-comparisons` (and no other leg), each scaled by what the same counter reads for the
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
@@ -58,6 +60,8 @@ def parse():
     ap.add_argument("--no-page-sizes", action="store_true", help="skip the 16/32/64-token page comparison")
     ap.add_argument("--no-shared-prefix", action="store_true", help="skip the shared-prefix decode comparison")
     ap.add_argument("--no-long-context", action="store_true", help="skip the 16 x 32k-token split-K decode")
+    ap.add_argument("--no-comparisons", action="store_true",
+                    help="skip the unfused step and the plain decode call (so that a profiler sees the step only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
     return ap.parse_args()
@@ -364,9 +368,13 @@ def main():
         ops.paged_gqa_decode(q, kc, vc, tables, lens, bt.max_seq_len, bt.scale, partition_size=args.partition,
                              out=out, workspace=ws)
 
-    def step():
+    def step_unfused():
         ops.reshape_and_cache(nk, nv, kc, vc, tables, lens, qsl)
         decode()
+
+    def step():
+        ops.paged_gqa_decode_append(q, nk, nv, kc, vc, tables, lens, bt.max_seq_len, bt.scale,
+                                    partition_size=args.partition, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -380,17 +388,23 @@ def main():
     kv_bytes = bt.kv_bytes()
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: the decode launch, timed with HIP events on its stream
-    decode_ms = event_time_ms(decode, max(20, args.steps // 2), stream)
-    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    # dominant kernel: the step's call, timed with HIP events on its stream
+    reps = max(20, args.steps // 2)
+    call_ms = event_time_ms(step, reps, stream)
+    achieved = kv_bytes / (call_ms * 1e-3) / 1e9
     traffic = None
     if DECODE_TRAFFIC is not None and DECODE_TRAFFIC["sources_sha256"] == decode_sources_sha256() \
             and args.partition == DECODE_TRAFFIC["partition_size"] and args.seed == DECODE_TRAFFIC["seed"]:
         traffic = DECODE_TRAFFIC["hbm_bytes_per_call"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_gqa_decode call (balanced decode kernel + merge kernel)", "avg_ms": round(decode_ms, 5),
-                "bytes_per_launch": kv_bytes}
+                "kernel": "paged_gqa_decode_append call (balanced decode kernel with the cache write fused + "
+                          "merge kernel)", "avg_ms": round(call_ms, 5), "bytes_per_launch": kv_bytes}
+    # the same step as two calls, and the attention call alone
+    unfused_ms = decode_ms = None
+    if not args.no_comparisons:
+        unfused_ms = event_time_ms(step_unfused, reps, stream)
+        decode_ms = event_time_ms(decode, reps, stream)
 
     record = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -399,9 +413,15 @@ def main():
                          "num_kv_heads": bt.num_kv_heads, "head_dim": bt.head_dim, "block_size": bt.block_size,
                          "context": "U{512..4096}", "sum_seq_len": int(bt.seq_lens.sum()), "seed": args.seed,
                          "partition_size": args.partition, "kv_dtype": "bf16", "out_dtype": "fp32",
-                         "step": "reshape_and_cache + paged_gqa_decode"},
+                         "step": "paged_gqa_decode_append (cache write fused into the decode)"},
               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
               "roofline": roofline}
+    if not args.no_comparisons:
+        record["unfused_step"] = {"calls": "reshape_and_cache + paged_gqa_decode", "ms": round(unfused_ms, 5),
+                                  "kv_gbs": round(kv_bytes / (unfused_ms * 1e-3) / 1e9, 2)}
+        record["decode_call"] = {"call": "paged_gqa_decode (no cache write)", "ms": round(decode_ms, 5),
+                                 "kv_gbs": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 2),
+                                 "hbm_frac": round(kv_bytes / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     if not args.no_mixed:
         mb = wl.mixed_chunked(seed=4)

@@ -74,13 +74,15 @@ bool use_stream(const gqa_dims& d, int32_t partition_size) {
 }
 
 // Balanced-decode workspace: [tile prefix, B + 1 ints][unit metadata, B * Hkv int4]
-// [segment outputs][segment lse].
+// [segment outputs][segment lse][whole-unit outputs, B * Hq * D][whole-unit lse, B * Hq]
+// (the last two serve the fused append).
 size_t stream_bytes(const gqa_dims& d, int workers) {
   const int G = d.num_heads / d.num_kv_heads;
   const size_t segs = (size_t)workers * 2 * G;
+  const size_t rows = (size_t)d.num_seqs * d.num_heads;
   return align_up((size_t)(d.num_seqs + 1) * sizeof(int)) +
          align_up((size_t)d.num_seqs * d.num_kv_heads * 4 * sizeof(int)) + align_up(segs * d.head_dim * sizeof(float)) +
-         align_up(segs * sizeof(float));
+         align_up(segs * sizeof(float)) + align_up(rows * d.head_dim * sizeof(float)) + align_up(rows * sizeof(float));
 }
 
 int device_workers(const gqa_dims& d) {
@@ -127,10 +129,15 @@ size_t mixed_bytes(const gqa_dims& d, int32_t num_tokens, int32_t max_seq_len, i
 }
 
 // Decode launch shared by paged_gqa_decode and the decode half of the mixed call.
+// new_key / new_value (decode only, query_start_loc null): a fused append of
+// each sequence's new token at position seq_lens[b] - 1 (the balanced decode
+// does it in its own launch; the other decompositions run the cache write
+// first).
 int run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
                int32_t num_tokens, int32_t max_seq_len, const gqa_dims& dims, float scale, int32_t partition_size,
-               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+               void* workspace, size_t workspace_bytes, hipStream_t stream, const void* new_key = nullptr,
+               const void* new_value = nullptr) {
   int psize = 0, nparts = 0;
   if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
   const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
@@ -154,6 +161,8 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.query_start_loc = query_start_loc;
+    a.new_key = new_key;
+    a.new_value = new_value;
     a.tile_prefix = reinterpret_cast<int*>(ws);
     ws += align_up((size_t)(dims.num_seqs + 1) * sizeof(int));
     a.unit_meta = reinterpret_cast<int4*>(ws);
@@ -161,6 +170,10 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     a.seg_out = reinterpret_cast<float*>(ws);
     ws += align_up(segs * dims.head_dim * sizeof(float));
     a.seg_lse = reinterpret_cast<float*>(ws);
+    ws += align_up(segs * sizeof(float));
+    a.unit_out = reinterpret_cast<float*>(ws);
+    ws += align_up((size_t)dims.num_seqs * dims.num_heads * dims.head_dim * sizeof(float));
+    a.unit_lse = reinterpret_cast<float*>(ws);
     a.num_seqs = dims.num_seqs;
     a.num_heads = dims.num_heads;
     a.num_kv_heads = dims.num_kv_heads;
@@ -169,15 +182,33 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     a.max_blocks_per_seq = dims.max_blocks_per_seq;
     a.num_tokens = num_tokens;
     a.num_workers = workers;
+    a.block_size = dims.block_size;
     a.scale_log2 = scale_log2;
     hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, stream);
     if (e != hipSuccess) return GQA_ERR_LAUNCH;
-    return status_from(gqa::launch_stream_reduce(a, dims.head_dim, out_f32, stream));
+    return status_from(gqa::launch_stream_reduce(a, dims.head_dim, kv_f32, out_f32, stream));
   }
 
   const size_t need = partial_bytes(dims, nparts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
   if (dims.num_seqs == 0) return GQA_OK;
+  if (new_key) {
+    gqa::CacheWriteArgs w;
+    w.key = new_key;
+    w.value = new_value;
+    w.key_cache = const_cast<void*>(key_cache);
+    w.value_cache = const_cast<void*>(value_cache);
+    w.block_tables = block_tables;
+    w.seq_lens = seq_lens;
+    w.query_start_loc = nullptr;          // token b is sequence b's new token
+    w.num_seqs = dims.num_seqs;
+    w.num_tokens = dims.num_seqs;
+    w.num_kv_heads = dims.num_kv_heads;
+    w.num_blocks = dims.num_blocks;
+    w.max_blocks_per_seq = dims.max_blocks_per_seq;
+    if (gqa::launch_cache_write(w, dims.head_dim, dims.block_size, dims.kv_dtype == GQA_F32, stream) != hipSuccess)
+      return GQA_ERR_LAUNCH;
+  }
   gqa::DecodeArgs a;
   a.out = out;
   a.query = query;
@@ -471,6 +502,22 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
   return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
                     max_seq_len, dims, scale, partition_size, workspace, workspace_bytes,
                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t paged_gqa_decode_append(void* out, const void* query, const void* key, const void* value, void* key_cache,
+                                void* value_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t max_seq_len, gqa_dims dims, float scale, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs > 0 &&
+      (!out || !query || !key || !value || !key_cache || !value_cache || !block_tables || !seq_lens))
+    return GQA_ERR_INVALID_ARG;
+  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
+                    max_seq_len, dims, scale, partition_size, workspace, workspace_bytes,
+                    reinterpret_cast<hipStream_t>(stream), key, value);
 }
 
 int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* partial_lse, const int32_t* seq_lens,

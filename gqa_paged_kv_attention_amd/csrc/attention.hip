@@ -42,6 +42,18 @@ __device__ __forceinline__ bool stream_is_decode(const StreamArgs& a, int b, int
   return q1 - q0 == 1 && q1 <= a.num_tokens && q0 >= 0;
 }
 
+__device__ __forceinline__ float load1f(const float* p) { return *p; }
+__device__ __forceinline__ float load1f(const uint16_t* p) { return bf16_bits_to_float(*p); }
+
+// Fused append (paged_gqa_decode_append), new token of sequence b at position
+// L - 1 = seq_lens[b] - 1: the decode reads keys [0, L - 1) from the pages and
+// masks that slot; the merge kernel folds the token in from new_key /
+// new_value and then stores it into its page slot, as reshape_and_cache would.
+// Sequence b of a fused append folds its new token (the pages hold the rest).
+__device__ __forceinline__ bool append_folds(const StreamArgs& a, int seq_len, int L) {
+  return a.new_key != nullptr && L > 0 && L == seq_len;
+}
+
 template <class Tile, int D, int NT, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void stream_decode_kernel(StreamArgs a) {
@@ -128,14 +140,17 @@ void stream_decode_kernel(StreamArgs a) {
     const int tile_end = (int)min((long long)nt, hi - unit0);
     int row;
     stream_is_decode(a, b, &row);
-    const int L = clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS);
+    const int sl = a.seq_lens[b];
+    const int L = clamp_len(sl, a.max_blocks_per_seq, Tile::kBS);
+    // fused append: the pages supply keys [0, L - 1); the merge kernel adds the new token
+    const int Lp = append_folds(a, sl, L) ? L - 1 : L;
 
     typename Tile::Q qf[NT];
     load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
     WaveState<Tile, NT> st;
     st.reset();
     run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                           a.num_blocks, a.num_kv_heads, kv, L, L - 1, tile_begin, tile_end, 1, a.scale_log2, lane);
+                           a.num_blocks, a.num_kv_heads, kv, Lp, Lp - 1, tile_begin, tile_end, 1, a.scale_log2, lane);
 
     const bool whole = tile_begin == 0 && tile_end == nt;
     const int slot = first ? 0 : 1;
@@ -145,7 +160,14 @@ void stream_decode_kernel(StreamArgs a) {
       const float lr = row_sum4(st.l[nt_]);
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       if (g < G) {
-        if (whole) {
+        if (whole && a.new_key) {
+          // fused append: every unit goes through the merge kernel
+          const size_t r = (size_t)b * a.num_heads + kv * G + g;
+          float* dst = a.unit_out + r * D + 4 * q;
+#pragma unroll
+          for (int dt = 0; dt < Tile::DT; ++dt) store4(dst + dt * 16, st.o[nt_][dt] * inv);
+          if (q == 0) a.unit_lse[r] = lr > 0.f ? (st.m[nt_] + __log2f(lr)) * kLn2 : -INFINITY;
+        } else if (whole) {
           OutT* dst = out + ((size_t)row * a.num_heads + kv * G + g) * D + 4 * q;
 #pragma unroll
           for (int dt = 0; dt < Tile::DT; ++dt) store4(dst + dt * 16, st.o[nt_][dt] * inv);
@@ -167,50 +189,136 @@ void stream_decode_kernel(StreamArgs a) {
 // output channel.  The work-group reads its unit's metadata and, if the unit's
 // tiles span several workers, combines their segments in worker order
 // (reproducible), folding kMergeBatch segments at a time with independent loads
-// and an online log-sum-exp: two memory round trips in all.
+// and an online log-sum-exp: two memory round trips in all.  In a fused append
+// every unit comes here (a whole unit as its one fp32 partial), and the new
+// token is one more term: log-weight scale * q.k_new, value v_new, loaded
+// beside the partials.
 constexpr int kMergeBatch = 8;
 
-template <int D, class OutT>
+// Fused append, the work-group of (unit b * Hkv + kv, row 0) in the merge
+// kernel: the new token into its page slot (a missing page leaves it
+// unwritten), thread d taking channel d.  The key row is token-major, so the
+// threads' elements are one contiguous store.  In the channel-major value page
+// the token's elements lie one per channel row; each thread rewrites the whole
+// 32-byte sector around its element (the slot patched in registers) instead of
+// storing the element alone, which memory serves as a partial-sector write.
+// No kernel of the call reads the slot, and the sector's other tokens are the
+// sequence's own, which nothing writes while it appends.
+template <int D, class T>
+__device__ __forceinline__ void append_store(const StreamArgs& a, int b, int kv, int d) {
+  const int pos = a.seq_lens[b] - 1;
+  const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / a.block_size];
+  if ((unsigned)page >= (unsigned)a.num_blocks) return;
+  const int slot = pos % a.block_size;
+  const T* kn = reinterpret_cast<const T*>(a.new_key) + ((size_t)b * a.num_kv_heads + kv) * D;
+  const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)b * a.num_kv_heads + kv) * D;
+  const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)a.block_size * D;
+  T* kcache = const_cast<T*>(reinterpret_cast<const T*>(a.key_cache)) + pbase;
+  T* vcache = const_cast<T*>(reinterpret_cast<const T*>(a.value_cache)) + pbase;
+  kcache[(size_t)slot * D + d] = kn[d];
+  constexpr int EPS = 32 / sizeof(T);                  // elements per 32-byte sector
+  T* sec = vcache + (size_t)d * a.block_size + (slot & ~(EPS - 1));
+  const uint4 lo = ld16(sec), hi = ld16(sec + EPS / 2);
+  uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  // patch element slot mod EPS (selects on the eight 32-bit words, no indexed array)
+  const int k = slot & (EPS - 1);
+  uint32_t bits, mask;
+  int word;
+  if constexpr (sizeof(T) == 2) {
+    word = k >> 1;
+    const int sh = (k & 1) * 16;
+    bits = (uint32_t)*reinterpret_cast<const uint16_t*>(vn + d) << sh;
+    mask = 0xFFFFu << sh;
+  } else {
+    word = k;
+    bits = *reinterpret_cast<const uint32_t*>(vn + d);
+    mask = 0xFFFFFFFFu;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = (j == word) ? ((w[j] & ~mask) | bits) : w[j];
+  *reinterpret_cast<uint4*>(sec) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(sec + EPS / 2) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+template <int D, class OutT, class InT>
 __global__ __launch_bounds__(D) void stream_reduce_kernel(StreamArgs a) {
+  __shared__ float s_dot[D / kWave];
   const int u = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
   const int4 m = a.unit_meta[u];
   const long long T = a.tile_prefix[a.num_seqs];
   const int w0 = m.x, w1 = m.y, slot0 = m.z, row = m.w;
-  if (w1 <= w0) return;
-  const int kv = u % a.num_kv_heads;
+  if (row < 0 || (w1 <= w0 && !a.new_key)) return;     // no keys, or written by the decode kernel
+  const int b = u / a.num_kv_heads, kv = u % a.num_kv_heads;
   const int G = a.group, W = a.num_workers;
+  const size_t r = (size_t)b * a.num_heads + kv * G + g;
+  float qk = 0.f, vn = 0.f;
+  bool fold = false;
+  if (a.new_key) {
+    // loaded beside the partials (valid addresses whether or not the sequence folds)
+    const int sl = a.seq_lens[b];
+    fold = append_folds(a, sl, clamp_len(sl, a.max_blocks_per_seq, a.block_size));
+    qk = load1f(reinterpret_cast<const InT*>(a.query) + ((size_t)row * a.num_heads + kv * G + g) * D + d) *
+         load1f(reinterpret_cast<const InT*>(a.new_key) + ((size_t)b * a.num_kv_heads + kv) * D + d);
+    vn = load1f(reinterpret_cast<const InT*>(a.new_value) + ((size_t)b * a.num_kv_heads + kv) * D + d);
+  }
   float M = -INFINITY, den = 0.f, acc = 0.f;
-  for (int wb = w0; wb <= w1; wb += kMergeBatch) {
-    float lv[kMergeBatch], ov[kMergeBatch];
+  if (w1 <= w0) {
+    // a whole unit of a fused append: its normalised output and log-sum-exp
+    M = a.unit_lse[r];
+    den = M == -INFINITY ? 0.f : 1.f;
+    acc = M == -INFINITY ? 0.f : a.unit_out[r * D + d];
+  } else {
+    for (int wb = w0; wb <= w1; wb += kMergeBatch) {
+      float lv[kMergeBatch], ov[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const int w = wb + k;
-      // workers past the unit, or with an empty range, hold no segment; every
-      // range holds at least floor(T / W) items, so only T < W needs the
-      // (64-bit, slow) division
-      const bool has = w <= w1 && (T >= W || T * w / W != T * (w + 1) / W);
-      const size_t seg = ((size_t)w * 2 + (w == w0 ? slot0 : 0)) * G + g;
-      lv[k] = has ? a.seg_lse[seg] : -INFINITY;
-      ov[k] = has ? a.seg_out[seg * D + d] : 0.f;
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int w = wb + k;
+        // workers past the unit, or with an empty range, hold no segment; every
+        // range holds at least floor(T / W) items, so only T < W needs the
+        // (64-bit, slow) division
+        const bool has = w <= w1 && (T >= W || T * w / W != T * (w + 1) / W);
+        const size_t seg = ((size_t)w * 2 + (w == w0 ? slot0 : 0)) * G + g;
+        lv[k] = has ? a.seg_lse[seg] : -INFINITY;
+        ov[k] = has ? a.seg_out[seg * D + d] : 0.f;
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lv[k]);
+      const float nm = fmaxf(M, bm);
+      const float nu = (nm == -INFINITY) ? 0.f : nm;
+      const float rr = fast_exp2((M - nu) * kLog2e);
+      den *= rr;
+      acc *= rr;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const float wgt = fast_exp2((lv[k] - nu) * kLog2e);
+        den += wgt;
+        acc += wgt == 0.f ? 0.f : wgt * ov[k];
+      }
+      M = nm;
     }
-    float bm = -INFINITY;
+  }
+  if (fold) {
+    // scale * q.k_new over the D threads: within each wave, then across waves
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lv[k]);
-    const float nm = fmaxf(M, bm);
-    const float nu = (nm == -INFINITY) ? 0.f : nm;
-    const float r = fast_exp2((M - nu) * kLog2e);
-    den *= r;
-    acc *= r;
+    for (int off = kWave / 2; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
+    if (D > kWave) {
+      if ((d & (kWave - 1)) == 0) s_dot[d / kWave] = qk;
+      __syncthreads();
+      qk = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const float wgt = fast_exp2((lv[k] - nu) * kLog2e);
-      den += wgt;
-      acc += wgt == 0.f ? 0.f : wgt * ov[k];
+      for (int i = 0; i < D / kWave; ++i) qk += s_dot[i];
     }
-    M = nm;
+    const float sn = qk * a.scale_log2 * kLn2;         // natural-log weight of the new token
+    const float nm = fmaxf(M, sn);
+    const float rr = fast_exp2((M - nm) * kLog2e);     // 0 while M = -inf
+    const float wn = fast_exp2((sn - nm) * kLog2e);
+    den = den * rr + wn;
+    acc = acc * rr + wn * vn;
   }
   OutT* out = reinterpret_cast<OutT*>(a.out);
   store1(out + ((size_t)row * a.num_heads + kv * G + g) * D + d, den > 0.f ? acc / den : 0.f);
+  if (fold && g == 0) append_store<D, InT>(a, b, kv, d);
 }
 
 template <int NTW>
@@ -408,15 +516,21 @@ hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_siz
   });
 }
 
-hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream) {
+template <class InT>
+void reduce_dispatch(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream) {
   const dim3 grid(a.num_kv_heads * a.num_seqs, a.group);
   if (head_dim == 64) {
-    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<64, float>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((stream_reduce_kernel<64, uint16_t>), grid, dim3(64), 0, stream, a);
+    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<64, float, InT>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((stream_reduce_kernel<64, uint16_t, InT>), grid, dim3(64), 0, stream, a);
   } else {
-    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<128, float>), grid, dim3(128), 0, stream, a);
-    else hipLaunchKernelGGL((stream_reduce_kernel<128, uint16_t>), grid, dim3(128), 0, stream, a);
+    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<128, float, InT>), grid, dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((stream_reduce_kernel<128, uint16_t, InT>), grid, dim3(128), 0, stream, a);
   }
+}
+
+hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream) {
+  if (kv_f32) reduce_dispatch<float>(a, head_dim, out_f32, stream);
+  else reduce_dispatch<uint16_t>(a, head_dim, out_f32, stream);
   return hipGetLastError();
 }
 

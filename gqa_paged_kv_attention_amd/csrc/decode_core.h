@@ -163,7 +163,8 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
                                           const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
                                           int L, int lim, int it0, int it1, int step, float scale_log2, int lane) {
   if (it0 >= it1) return;
-  const int npages = (L + Tile::kBS - 1) / Tile::kBS;
+  // at least one page: a fused append walks the tile of its only key with L = 0
+  const int npages = max(1, (L + Tile::kBS - 1) / Tile::kBS);
   if constexpr (!Tile::kPipelined) {
     for (int it = it0; it < it1; it += step) {
       typename Tile::K kf;

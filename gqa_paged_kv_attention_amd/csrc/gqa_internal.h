@@ -40,10 +40,14 @@ struct StreamArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* query_start_loc;   // nullptr: pure decode
+  const void* new_key;              // [B, Hkv, D] or nullptr: the step's new token of each sequence,
+  const void* new_value;            // written into the pages and attended from here (fused append)
   int* tile_prefix;                 // [B + 1]: prefix of tiles * Hkv (work-group 0 writes it)
   int4* unit_meta;                  // [B * Hkv]: {first worker, last worker, first slot, out row}
   float* seg_out;                   // [num_workers, 2, G, D]: cut segments, normalised
   float* seg_lse;                   // [num_workers, 2, G]
+  float* unit_out;                  // [B, Hq, D]: fused append, a whole unit's normalised output
+  float* unit_lse;                  // [B, Hq]: and its natural-log log-sum-exp
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -52,6 +56,7 @@ struct StreamArgs {
   int max_blocks_per_seq;
   int num_tokens;
   int num_workers;                  // 4 per work-group
+  int block_size;                   // tokens per page
   float scale_log2;
 };
 
@@ -98,7 +103,7 @@ struct CacheWriteArgs {
   void* value_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  const int32_t* query_start_loc;
+  const int32_t* query_start_loc;   // nullptr: token b is sequence b's single new token
   int num_seqs;
   int num_tokens;
   int num_kv_heads;
@@ -114,7 +119,7 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool
 int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs);
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
                                 hipStream_t stream);
-hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream);
+hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream);
 // Rows per prefill work-group (depends only on the build).
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,

@@ -43,11 +43,13 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
     vx = ld16(reinterpret_cast<const T*>(a.value) + src);
   }
   const int guess = min(tok, a.num_seqs - 1);
-  int q0 = a.query_start_loc[guess], q1 = a.query_start_loc[guess + 1];
+  // without query_start_loc, token t is sequence t's single new token
+  int q0 = a.query_start_loc ? a.query_start_loc[guess] : guess;
+  int q1 = a.query_start_loc ? a.query_start_loc[guess + 1] : guess + 1;
   int len = a.seq_lens[guess];
   int b = guess;
   const bool hit = q0 <= tok && tok < q1;
-  if (__syncthreads_and(hit || !active) == 0) {
+  if (a.query_start_loc && __syncthreads_and(hit || !active) == 0) {
     // some token of the work-group is not in its guessed sequence: search
     const bool staged = a.num_seqs <= kLdsSeqs;
     if (staged)

@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_decode_workspace_size.restype = sz
     lib.paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
     lib.paged_gqa_decode.restype = i32
+    lib.paged_gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
+    lib.paged_gqa_decode_append.restype = i32
     lib.splitk_lse_reduce.argtypes = [vp, vp, vp, vp, vp, Dims, i32, i32, i32, vp]
     lib.splitk_lse_reduce.restype = i32
     lib.chunked_prefill_paged_decode_workspace_size.argtypes = [Dims, i32, i32, i32]
@@ -194,6 +196,30 @@ def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_
                                                    _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
                                                    float(scale), int(partition_size), _ptr(ws), wsb,
                                                    _stream(stream)))
+    return out
+
+
+def paged_gqa_decode_append(query, key, value, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int,
+                            scale: float, partition_size: int = 0, out=None, out_dtype=None, workspace=None,
+                            stream=None):
+    """One decode step with the cache write fused: ``key``/``value [B, Hkv, d]`` (each sequence's new
+    token, at position seq_lens[b] - 1) go into the caches, and ``query [B, Hq, d]`` -> ``out [B, Hq, d]``
+    attends over all seq_lens[b] tokens."""
+    lib = load_library()
+    _check_device(query, key, value, key_cache, value_cache, block_tables, seq_lens, out, workspace)
+    _check_int32(block_tables, seq_lens)
+    B, Hq, d = query.shape
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=B, num_heads=Hq, key_cache=key_cache, block_tables=block_tables, q_dtype=query.dtype,
+                     out_dtype=out_dtype)
+    nbytes = int(lib.paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
+    _call("paged_gqa_decode_append",
+          lib.paged_gqa_decode_append(_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache),
+                                      _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
+                                      float(scale), int(partition_size), _ptr(ws), wsb, _stream(stream)))
     return out
 
 

@@ -154,6 +154,36 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
                          size_t workspace_bytes, void* stream);
 
 /*
+ * paged_gqa_decode_append: one decode step with the cache write fused in.
+ * key/value [num_seqs, num_kv_heads, head_dim] (kv_dtype, device) hold each
+ * sequence's new token, at position seq_lens[b] - 1 (seq_lens counts it).
+ * The call writes it into the caches exactly as reshape_and_cache with
+ * query_start_loc = [0, 1, ..., num_seqs] does, and returns the attention of
+ * paged_gqa_decode over all seq_lens[b] tokens, the new one included ("[Performance]
+ * Use optimized kernels for MQA/GQA", opening post, item 2: the step's keys and
+ * values go into the paged cache that the decode then reads).
+ *
+ * Same dims, dtypes, page sizes, partition_size meaning and workspace
+ * (paged_gqa_decode_workspace_size) as paged_gqa_decode.  With the balanced
+ * split it is the same two launches as paged_gqa_decode and no more: the
+ * decode kernel reads keys [0, seq_lens[b] - 1) from the pages, and the merge
+ * kernel adds the new token's term from key/value and stores key/value into
+ * the pages.  The other decompositions run the cache write, then the decode.
+ * Precondition of the balanced path (as in any paged allocator): the page
+ * that receives a sequence's new token holds no other sequence's new token.
+ * The caches end bit-identical to
+ * reshape_and_cache's; the output agrees with reshape_and_cache followed by
+ * paged_gqa_decode up to fp32 rounding.  seq_lens[b] == 0: nothing is written
+ * and the output row is zero.  Errors as paged_gqa_decode, plus
+ * GQA_ERR_INVALID_ARG for a null key or value.
+ */
+int32_t paged_gqa_decode_append(void* out, const void* query, const void* key, const void* value,
+                                void* key_cache, void* value_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t max_seq_len, gqa_dims dims, float scale,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * splitk_lse_reduce: merge per-partition decode results.
  *   partial_out [num_seqs, num_heads, max_partitions, head_dim] fp32: the
  *                partition's normalised output;

@@ -27,7 +27,8 @@ FAKE = ctypes.c_void_p(0x1000)    # never dereferenced: every call below fails v
 
 def test_every_declared_symbol_is_exported(lib):
     names = ops.declared_functions()
-    assert {"reshape_and_cache", "paged_gqa_decode", "splitk_lse_reduce", "chunked_prefill_paged_decode",
+    assert {"reshape_and_cache", "paged_gqa_decode", "paged_gqa_decode_append", "splitk_lse_reduce",
+            "chunked_prefill_paged_decode",
             "paged_gqa_decode_workspace_size", "chunked_prefill_paged_decode_workspace_size",
             "paged_cross_attention", "paged_cross_attention_workspace_size",
             "paged_gqa_decode_shared_prefix", "paged_gqa_decode_shared_prefix_workspace_size",
@@ -98,6 +99,24 @@ def test_workspace_size_and_check(lib):
     assert decode(lib, d, max_seq_len=4096, partition=0, ws=FAKE, wsb=256) == WORKSPACE
 
 
+def append(lib, d, key=FAKE, value=FAKE, ptr=FAKE, max_seq_len=256, partition=0, ws=None, wsb=0, scale=0.1):
+    return lib.paged_gqa_decode_append(ptr, ptr, key, value, ptr, ptr, ptr, ptr, max_seq_len, d, scale, partition,
+                                       ws, wsb, None)
+
+
+def test_decode_append_validation(lib):
+    """The fused append checks what paged_gqa_decode checks, plus its key and
+    value rows; it takes paged_gqa_decode's workspace."""
+    assert append(lib, dims(), key=None) == INVALID
+    assert append(lib, dims(), value=None) == INVALID
+    assert append(lib, dims(), partition=48) == INVALID
+    assert append(lib, dims(), scale=float("inf")) == INVALID
+    assert append(lib, dims(head_dim=96)) == UNSUPPORTED
+    assert append(lib, dims(num_seqs=0), key=None, value=None, ptr=None) == OK
+    assert append(lib, dims(), max_seq_len=4096, partition=512) == WORKSPACE
+    assert append(lib, dims(), max_seq_len=4096, partition=0, ws=FAKE, wsb=256) == WORKSPACE
+
+
 def test_empty_batches_return_ok_without_launch(lib):
     assert decode(lib, dims(num_seqs=0), ptr=None) == OK
     assert lib.reshape_and_cache(None, None, None, None, None, None, None, 0, dims(), None) == OK
@@ -117,17 +136,17 @@ def test_mixed_and_reduce_validation(lib):
 
 
 def test_mixed_bf16_workspace(lib):
-    """bf16 mixed batches need the scheduled unit list (32 bytes per unit, at
+    """bf16 mixed batches need the scheduled unit list (64 bytes per unit, at
     least num_tokens * G / 128 prefill row tiles plus one unit per decode), a
     count, and partials only when decodes are split; a batch of decodes only
     runs the decode, so the decode's workspace fits as well."""
     d = dims()                                     # 4 seqs, G = 4, bf16
     n = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 256, 0)
-    assert n % 256 == 0 and n >= (1000 * 4 // 128 + 4) * 32 + 4
+    assert n % 256 == 0 and n >= (1000 * 4 // 128 + 4) * 64 + 4
     assert n >= lib.paged_gqa_decode_workspace_size(d, 256, 0)
     # a split adds the partials of 16 partitions per (sequence, query head)
     split = lib.chunked_prefill_paged_decode_workspace_size(d, 1000, 8192, 512)
-    assert split >= (1000 * 4 // 128 + 4 * 17) * 32 + 4 * 32 * 16 * 128 * 4
+    assert split >= (1000 * 4 // 128 + 4 * 17) * 64 + 4 * 32 * 16 * 128 * 4
     assert split >= lib.paged_gqa_decode_workspace_size(d, 8192, 512)
     call = lambda ws, wsb: lib.chunked_prefill_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 100, 256,
                                                             d, 0.1, 0, ws, wsb, None)
