@@ -42,7 +42,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "996decda1c96876765a7996d8fe7b08379f0812e0461f0cad713ad483d5f6723", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 645914871, "write_bytes_per_call": 6333030, "hbm_bytes_per_call": 652247901, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "b53c453eaee6bf13f6f1978b324f4aa7a6a2a2173172836465c37d7589cf07ab", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648480276, "write_bytes_per_call": 8562381, "hbm_bytes_per_call": 657042657, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
