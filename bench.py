@@ -13,8 +13,9 @@ Also reported: the decode kernel's roofline (HIP events on its launch
 stream), the mixed chunked-prefill + decode batch's tokens/s, the GQA saving
 against the same cache expanded per query head, cross-attention over a static
 encoder cache, the decode per page size, the shared-prefix decode against the
-plain decode, the 16 x 32k-token split-K decode, and the CPU oracle's
-throughput on a bounded sample as a baseline.
+plain decode, the 16 x 32k-token split-K decode, reshape_and_cache alone on
+the decode step and on the mixed batch, and the CPU oracle's throughput on a
+bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
        python bench.py --copy-calibration   (a plain 512 MiB device copy, for
@@ -60,6 +61,7 @@ def parse():
     ap.add_argument("--no-page-sizes", action="store_true", help="skip the 16/32/64-token page comparison")
     ap.add_argument("--no-shared-prefix", action="store_true", help="skip the shared-prefix decode comparison")
     ap.add_argument("--no-long-context", action="store_true", help="skip the 16 x 32k-token split-K decode")
+    ap.add_argument("--no-cache-write", action="store_true", help="skip the reshape_and_cache leg")
     ap.add_argument("--no-comparisons", action="store_true",
                     help="skip the unfused step and the plain decode call (so that a profiler sees the step only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -251,6 +253,29 @@ def long_context_leg(dev, stream, reps):
                                                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del ws
     del q, kc, vc, out
+    return res
+
+
+def cache_write_leg(dev, stream, reps, seed):
+    """reshape_and_cache alone: the decode step's 64 new tokens and the mixed
+    batch's 8166 (prefill chunks and decodes), each token's K and V rows read
+    once and written once (2 * Hkv * d * 2 bytes each way per token)."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+
+    res = {}
+    for name, bt in (("decode_step", wl.llama31_8b_decode(seed=seed)), ("mixed_batch", wl.mixed_chunked(seed=4))):
+        up = lambda a: ops.to_device(a, dev)
+        nk, nv, kc, vc = up(bt.new_key), up(bt.new_value), up(bt.key_cache), up(bt.value_cache)
+        tb, sl, qsl = up(bt.block_tables), up(bt.seq_lens), up(bt.query_start_loc)
+        f = lambda: ops.reshape_and_cache(nk, nv, kc, vc, tb, sl, qsl)
+        warm_up(f, stream)
+        ms = event_time_ms(f, reps, stream)
+        nbytes = 2 * bt.num_tokens * 2 * bt.num_kv_heads * bt.head_dim * bt.kv_itemsize   # read + written
+        res[name] = {"tokens": bt.num_tokens, "us": round(ms * 1e3, 2), "bytes": nbytes,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        del nk, nv, kc, vc
     return res
 
 
@@ -475,6 +500,9 @@ def main():
 
     if not args.no_long_context:
         record["long_context"] = long_context_leg(dev, stream, 20)
+
+    if not args.no_cache_write:
+        record["cache_write"] = cache_write_leg(dev, stream, 50, args.seed)
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(bt, args.cpu_seconds)
