@@ -57,9 +57,10 @@ __device__ __forceinline__ bool append_folds(const StreamArgs& a, int seq_len, i
 template <class Tile, int D, int NT, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void stream_decode_kernel(StreamArgs a) {
-  extern __shared__ int s_pref[];          // [B + 1] exclusive prefix of tiles * Hkv
+  extern __shared__ int s_pref[];          // [B + 1] exclusive prefix of tiles * Hkv, then s_len
   __shared__ int s_scan[kWaves];
   const int B = a.num_seqs, G = a.group;
+  int* s_len = s_pref + B + 1;             // [B]: keys each decode reads from the pages
   const int lane = lane_id();
   const int n = lane & 15, q = lane >> 4;
   OutT* out = reinterpret_cast<OutT*>(a.out);
@@ -72,8 +73,11 @@ void stream_decode_kernel(StreamArgs a) {
     if (b < B) {
       int row;
       const bool dec = stream_is_decode(a, b, &row);
-      const int L = dec ? clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS) : 0;
+      const int sl = a.seq_lens[b];
+      const int L = dec ? clamp_len(sl, a.max_blocks_per_seq, Tile::kBS) : 0;
       v = (L + kTile - 1) / kTile * a.num_kv_heads;
+      // fused append: the pages supply keys [0, L - 1); the merge kernel adds the new token
+      s_len[b] = append_folds(a, sl, L) ? L - 1 : L;
       if (dec && L == 0 && (b % gridDim.x) == (int)blockIdx.x) {
         // an empty decode sequence has a zero output row
         for (int i = 0; i < a.num_heads * D; ++i) store1(out + (size_t)row * a.num_heads * D + i, 0.f);
@@ -140,10 +144,7 @@ void stream_decode_kernel(StreamArgs a) {
     const int tile_end = (int)min((long long)nt, hi - unit0);
     int row;
     stream_is_decode(a, b, &row);
-    const int sl = a.seq_lens[b];
-    const int L = clamp_len(sl, a.max_blocks_per_seq, Tile::kBS);
-    // fused append: the pages supply keys [0, L - 1); the merge kernel adds the new token
-    const int Lp = append_folds(a, sl, L) ? L - 1 : L;
+    const int Lp = s_len[b];                 // from the prefix pass: no dependent load before the page ids
 
     typename Tile::Q qf[NT];
     load_group_query<Tile, D, NT>(qf, a.query, row, a.num_heads, kv, G, lane);
@@ -493,7 +494,7 @@ int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int 
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    const size_t lds = (size_t)(num_seqs + 1) * sizeof(int);
+    const size_t lds = (size_t)(2 * num_seqs + 1) * sizeof(int);
     with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [&](void (*k)(StreamArgs)) {
       int blocks = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(k), kThreads, lds) ==
@@ -508,7 +509,7 @@ int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int 
 
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
                                 hipStream_t stream) {
-  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
   const dim3 grid(a.num_workers / kWaves), block(kThreads);
   return with_stream_kernel(head_dim, block_size, kv_f32, out_f32, a.group, [&](void (*k)(StreamArgs)) {
     hipLaunchKernelGGL(k, grid, block, lds, stream, a);

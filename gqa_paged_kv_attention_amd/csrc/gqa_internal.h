@@ -30,7 +30,7 @@ struct DecodeArgs {
 
 // Balanced ("stream") decode: persistent waves, each owning an equal slice of
 // the list of (sequence, kv head, 32-token tile) work items.
-constexpr int kMaxStreamSeqs = 15871;   // prefix table fits 62 KiB of LDS
+constexpr int kMaxStreamSeqs = 7935;    // prefix and length tables fit 62 KiB of LDS
 constexpr int kStreamWorkersPerGroup = 4;
 struct StreamArgs {
   void* out;

@@ -127,7 +127,7 @@ int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, v
  * head) whose keys fall in one range is finished by that wave, one cut by
  * range boundaries is merged by log-sum-exp in a second, small kernel, in a
  * fixed order (results are reproducible on a given device).  Otherwise (many
- * units, G > 16, num_seqs > 15871, or more than 2^31 tiles) each (sequence,
+ * units, G > 16, num_seqs > 7935, or more than 2^31 tiles) each (sequence,
  * kv head) is one work-group's job, with no split.
  *
  * partition_size > 0: fixed split-K.  Each sequence of L tokens is split into
