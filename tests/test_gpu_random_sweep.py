@@ -12,7 +12,7 @@ import torch
 
 from gqa_paged_kv_attention_amd import ops
 from gqa_paged_kv_attention_amd import workloads as wl
-from oracle import decode_ref, paged_attention_ref
+from oracle import cache_write_ref, decode_ref, paged_attention_ref
 from tests.gpu_util import DeviceBatch, assert_parity, have_gpu, host, poison_tails
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -49,6 +49,34 @@ def test_random_decode(seed):
     ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
                      bt.scale)
     assert_parity(got, ref, bt.dtype, f"{bt.describe()} P={partition}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_decode_append(seed):
+    """The fused append: caches bit-exact against the oracle's cache write of
+    each sequence's new token (none for an empty sequence), output at the bar
+    against the oracle's decode over them."""
+    rng, shape = draw(300 + seed)
+    B = int(rng.integers(1, 24))
+    L = lengths(rng, B, 1500)
+    bt = wl.make_batch(name="rnd_app", seed=seed, seq_lens=L, query_lens=np.minimum(L, 1), poison_slack=True,
+                       **shape)
+    bt.query = wl._normal_storage(rng, (B, shape["num_heads"], shape["head_dim"]), shape["dtype"])
+    rows = (B, shape["num_kv_heads"], shape["head_dim"])
+    nk, nv = wl._normal_storage(rng, rows, shape["dtype"]), wl._normal_storage(rng, rows, shape["dtype"])
+    has = L > 0
+    qsl = np.concatenate([[0], np.cumsum(has)])
+    kc, vc = cache_write_ref(nk[has], nv[has], bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, qsl)
+    ref = decode_ref(bt.query, kc, vc, bt.block_tables, bt.seq_lens, bt.num_kv_heads, bt.scale)
+    dev = DeviceBatch(bt)
+    partition = int(rng.choice([0, 0, 64, 256]))
+    got = ops.paged_gqa_decode_append(dev.query, ops.to_device(nk), ops.to_device(nv), dev.key_cache, dev.value_cache,
+                                      dev.block_tables, dev.seq_lens, bt.max_seq_len, bt.scale,
+                                      partition_size=partition)
+    torch.cuda.synchronize()
+    assert np.array_equal(ops.to_host_storage(dev.key_cache).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(ops.to_host_storage(dev.value_cache).view(np.uint8), vc.view(np.uint8))
+    assert_parity(host(got), ref, bt.dtype, f"{bt.describe()} P={partition}")
 
 
 @pytest.mark.parametrize("seed", range(12))
