@@ -147,7 +147,7 @@ constexpr int kUnitEmpty = -1;
 constexpr int kUnitWholeGroup = -2;
 // Decode partitions of more 32-token tiles than this are run by a whole
 // work-group (its waves take the tiles round-robin); shorter ones by one wave.
-constexpr int kWaveDecodeMaxTiles = 32;
+constexpr int kWaveDecodeMaxTiles = 64;
 struct ScheduleArgs {
   const int32_t* seq_lens;
   const int32_t* block_tables;

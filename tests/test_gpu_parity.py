@@ -277,16 +277,16 @@ def test_mixed_long_decodes_split_by_library(dtype):
 
 @pytest.mark.parametrize("n_short", [1, 2, 3, 4, 5, 9])
 def test_mixed_decode_packs(n_short):
-    """Decode partitions of at most 32 tiles run one per wave, four to a
+    """Decode partitions of at most 64 tiles run one per wave, four to a
     work-group; longer ones run on a whole work-group.  n_short short decodes
-    leave the last pack with 1..4 partitions; lengths at the 32-tile boundary
-    (1024 keys: packed; 1025: whole work-group) and empty and one-key decodes
+    leave the last pack with 1..4 partitions; lengths at the 64-tile boundary
+    (2048 keys: packed; 2049: whole work-group) and empty and one-key decodes
     sit beside prefill chunks."""
     rng = np.random.default_rng(90 + n_short)
-    short = list(rng.integers(1, 1025, size=n_short))
-    short[0] = 1024
+    short = list(rng.integers(1, 2049, size=n_short))
+    short[0] = 2048
     q_lens = [1] * n_short + [1, 1, 1, 40, 3]
-    seq_lens = short + [1025, 1, 2900, 300, 45]
+    seq_lens = short + [2049, 1, 5000, 300, 45]
     q_lens.append(0)
     seq_lens.append(5)
     bt = wl.make_batch(name="packs", seed=91 + n_short, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
