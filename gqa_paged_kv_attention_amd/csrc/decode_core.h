@@ -297,9 +297,22 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
 
   WaveState<Tile, NT> st;
   st.reset();
-  run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                         a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0 + w, tile0 + n_tiles, kWaves,
-                         a.scale_log2, lane);
+  if constexpr (NT == 1) {
+    // each wave a contiguous quarter of the partition's tiles, walked in pairs
+    // (two tiles per round trip); measured faster than round-robin tiles for
+    // G <= 16 (Llama-3.1-8B shapes at 512-token partitions 148.8 -> 141.3 us)
+    const int wper = n_tiles / kWaves, wextra = n_tiles % kWaves;
+    const int wb = tile0 + w * wper + min(w, wextra);
+    const int we = wb + wper + (w < wextra ? 1 : 0);
+    run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
+                           a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, wb, we, 1, a.scale_log2, lane);
+  } else {
+    // two row blocks per wave (G > 16): tiles round-robin over the waves, which
+    // was faster there (MQA, G = 32: 19.4 vs 20.5 us)
+    run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
+                           a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0 + w, tile0 + n_tiles, kWaves,
+                           a.scale_log2, lane);
+  }
 
   // ---- merge the four waves ----
   float (*sm_m)[R] = reinterpret_cast<float (*)[R]>(lds);
