@@ -43,7 +43,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
 # sources it was measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "95e53abb97988af111c786a1906d00143c21e11aac26a535e274c25848ff3b44", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648800525, "write_bytes_per_call": 8563405, "hbm_bytes_per_call": 657363930, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "a4c9c579bb51148e2a11858c07847a832d6afc625ec6468c9c93bfc6c5116258", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648800525, "write_bytes_per_call": 8563405, "hbm_bytes_per_call": 657363930, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():

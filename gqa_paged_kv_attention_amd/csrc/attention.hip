@@ -49,7 +49,8 @@ __device__ __forceinline__ float load1f(const uint16_t* p) { return bf16_bits_to
 // L - 1 = seq_lens[b] - 1: the decode reads keys [0, L - 1) from the pages and
 // masks that slot; the merge kernel folds the token in from new_key /
 // new_value and then stores it into its page slot, as reshape_and_cache would.
-// Sequence b of a fused append folds its new token (the pages hold the rest).
+// True when sequence b (seq_lens[b] = seq_len, L = seq_len clamped to its
+// block-table row) takes that path.
 __device__ __forceinline__ bool append_folds(const StreamArgs& a, int seq_len, int L) {
   return a.new_key != nullptr && L > 0 && L == seq_len;
 }
