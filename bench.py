@@ -359,7 +359,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: multi-GPU runs are not part of this build "
+        print("bench.py measures one GPU only: this library runs on one GPU; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
         sys.exit(2)
 
