@@ -102,7 +102,11 @@ int32_t gqa_version(void);
  * position pos = seq_lens[b] - q_len + j, i.e. page block_tables[b][pos / bs],
  * slot pos % bs.  A bit-exact copy in the cache dtype (kv_dtype; key/value are
  * in kv_dtype too).  Slots not written are left untouched.  num_tokens may be 0
- * (no launch).  ("[Performance] Use optimized kernels for MQA/GQA", opening
+ * (no launch).  When the batch has more new tokens than sequences (prefill
+ * chunks), each 16-position run of a value page's channel row is rewritten
+ * whole around the new tokens (its other slots with the values they hold), so
+ * a page that receives one sequence's new tokens must not receive another
+ * sequence's in the same call (a paged allocator never does that).  ("[Performance] Use optimized kernels for MQA/GQA", opening
  * post: incoming keys/values are [tokens, num_kv_heads, head]; item 2: the
  * decode reads them back from a paged cache.)
  */
