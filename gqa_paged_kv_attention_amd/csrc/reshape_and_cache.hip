@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
 // new tokens receives no other sequence's.  The work-group finds its
 // sequence by a scan of the per-sequence group counts, D sequences at a time.
 constexpr int kGroup = 16;
+constexpr int kGroupMaxSeqs = 1024;
 
 template <int D, int BS, class T>
 __global__ __launch_bounds__(D) void cache_write_group_kernel(CacheWriteArgs a) {
@@ -182,9 +183,12 @@ __global__ __launch_bounds__(D) void cache_write_group_kernel(CacheWriteArgs a) 
 
 template <class T>
 hipError_t dispatch(const CacheWriteArgs& a, int D, int block_size, hipStream_t s) {
-  // One new token per sequence at most (a decode step): one thread per 16-byte
-  // chunk, two dependent loads.  Prefill chunks: the grouped kernel.
-  if (!a.query_start_loc || a.num_tokens <= a.num_seqs) {
+  // A decode step, or few new tokens per sequence, or so many sequences that
+  // each work-group's scan of them would cost more than the stores it saves:
+  // one thread per 16-byte chunk, two dependent loads.  Prefill chunks (on
+  // average four or more new tokens per sequence, up to 1024 sequences): the
+  // grouped kernel.
+  if (!a.query_start_loc || (long long)a.num_tokens < 4LL * a.num_seqs || a.num_seqs > kGroupMaxSeqs) {
     const long long total = (long long)a.num_tokens * a.num_kv_heads * (D * (long long)sizeof(T) / 16);
     const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
     return with_block_size(block_size, [&](auto bs) {

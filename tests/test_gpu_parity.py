@@ -45,13 +45,16 @@ def mixed_step(bt, partition_size, out_dtype=torch.float32):
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("kind", ["mixed", "decode", "one_chunk"])
+@pytest.mark.parametrize("kind", ["mixed", "decode", "one_chunk", "sparse_chunks"])
 def test_reshape_and_cache_bit_exact(dtype, d, kind):
-    """Mixed batches take the query_start_loc search; a decode step (token t is
-    sequence t) and a single chunk hit the direct lookup."""
+    """Batches with chunks (four or more new tokens per sequence on average)
+    take the grouped kernel; a decode step (token t is sequence t) and a batch
+    with few short chunks among many decodes take the per-chunk kernel, the
+    latter through its query_start_loc search."""
     rng = np.random.default_rng(7)
     q_lens = {"mixed": np.array([1, 5, 0, 17, 1, 33, 2]), "decode": np.ones(300, dtype=np.int64),
-              "one_chunk": np.array([70])}[kind]
+              "one_chunk": np.array([70]),
+              "sparse_chunks": np.array([1] * 30 + [3, 0, 5, 2] + [1] * 6)}[kind]
     seq_lens = q_lens + rng.integers(0, 40, size=len(q_lens))
     bt = wl.make_batch(name="rc", seed=8, num_heads=8, num_kv_heads=4, head_dim=d, block_size=16,
                        seq_lens=seq_lens, query_lens=q_lens, dtype=dtype)
