@@ -454,6 +454,21 @@ def test_full_mixed_sampled():
     check_rows(out, ref, rows, bt.dtype, bt.describe())
 
 
+@pytest.mark.parametrize("name", ["mixed", "decode"])
+def test_full_cache_write_bit_exact(name):
+    """reshape_and_cache at the benchmark's sizes (the mixed batch's 8166 new
+    tokens through the grouped kernel, the decode step's 64 through the
+    per-chunk kernel): both whole caches equal the oracle's, byte for byte."""
+    bt = wl.mixed_chunked(seed=4) if name == "mixed" else wl.llama31_8b_decode(seed=2)
+    dev = DeviceBatch(bt)
+    dev.cache_write()
+    torch.cuda.synchronize()
+    kc, vc = cache_write_ref(bt.new_key, bt.new_value, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                             bt.query_start_loc)
+    assert np.array_equal(ops.to_host_storage(dev.key_cache).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(ops.to_host_storage(dev.value_cache).view(np.uint8), vc.view(np.uint8))
+
+
 def test_full_longctx_splitk_sampled():
     bt = wl.longctx_splitk(seed=5)
     seqs = [0, 7, 15]
