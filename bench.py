@@ -139,6 +139,16 @@ def cold_times_ms(fn, reps, stream, flush):
     return {"p10_ms": round(float(p10), 5), "p50_ms": round(float(p50), 5), "p90_ms": round(float(p90), 5)}
 
 
+def stream_copy_gbs(buf, stream, reps=20):
+    """HBM bandwidth of a plain device copy here: one half of `buf` (1 GiB)
+    copied into the other, 512 MiB read + 512 MiB written, GB/s of bytes moved."""
+    half = buf.numel() // 2
+    src, dst = buf[:half], buf[half:]
+    f = lambda: dst.copy_(src)
+    warm_up(f, stream, 10.0)
+    return round(buf.numel() * buf.element_size() / (event_time_ms(f, reps, stream) * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(bt, seconds):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same workload.
 
@@ -455,6 +465,10 @@ def main():
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     roofline["cold"] = dict(cold_times_ms(step, 20, stream, flush),
                             note="each call alone after a 1 GiB read (caches flushed); achieved uses back-to-back calls")
+    # the same achieved rate against a plain device copy's
+    copy_gbs = stream_copy_gbs(flush, stream)
+    roofline["measured_copy"] = {"gbs": copy_gbs, "frac": round(achieved / copy_gbs, 4),
+                                 "kernel": "torch copy_ of 512 MiB (read + write)"}
     # the same step as two calls, and the attention call alone
     unfused_ms = decode_ms = None
     if not args.no_comparisons:
