@@ -139,6 +139,33 @@ def cold_times_ms(fn, reps, stream, flush):
     return {"p10_ms": round(float(p10), 5), "p50_ms": round(float(p50), 5), "p90_ms": round(float(p90), 5)}
 
 
+def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
+    """chunked_prefill_paged_decode on the sequences `idx` of the mixed batch
+    alone (their query rows, block-table rows and lengths; the same caches and
+    pages), bf16 output: ms per call."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    idx = np.asarray(idx, dtype=np.int64)
+    ql = mb.query_lens.astype(np.int64)[idx]
+    qsl = mb.query_start_loc.astype(np.int64)
+    sub_qsl = np.zeros(len(idx) + 1, np.int32)
+    sub_qsl[1:] = np.cumsum(ql)
+    rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in idx])
+    sel = lambda t, ix: t[torch.from_numpy(ix).to(dev)].contiguous()
+    q, tb, sl = sel(mq, rows), sel(mt, idx), sel(ml, idx)
+    s_qsl = ops.to_device(sub_qsl, dev)
+    T = int(sub_qsl[-1])
+    max_sl = int(mb.seq_lens[idx].max())
+    out = torch.empty(T, mb.num_heads, mb.head_dim, dtype=torch.bfloat16, device=dev)
+    dims = ops.make_dims(num_seqs=len(idx), num_heads=mb.num_heads, key_cache=mkc, block_tables=tb, q_dtype=q.dtype,
+                         out_dtype=out.dtype)
+    ws = torch.zeros(max(ops.mixed_workspace_size(dims, T, max_sl, 0), 1), dtype=torch.uint8, device=dev)
+    f = lambda: ops.chunked_prefill_paged_decode(q, mkc, mvc, tb, sl, s_qsl, int(ql.max()), max_sl, mb.scale,
+                                                 partition_size=0, out=out, workspace=ws)
+    warm_up(f, stream)
+    return event_time_ms(f, reps, stream)
+
+
 def stream_copy_gbs(buf, stream, reps=20):
     """HBM bandwidth of a plain device copy here: one half of `buf` (1 GiB)
     copied into the other, 512 MiB read + 512 MiB written, GB/s of bytes moved."""
@@ -518,6 +545,13 @@ def main():
             warm_up(mixed, stream)
             times[name] = event_time_ms(mixed, 50, stream)
         mixed_ms = times["bf16"]
+        # diagnostics: each part of the batch alone through the same entry point
+        pf_idx, dec_idx = np.where(ql > 1)[0], np.where(ql == 1)[0]
+        pf_flops = 4 * mb.head_dim * mb.num_heads * int(np.sum(ql[pf_idx] * prior[pf_idx] +
+                                                                ql[pf_idx] * (ql[pf_idx] + 1) // 2))
+        dec_kv = int(mb.seq_lens[dec_idx].astype(np.int64).sum()) * 2 * mb.num_kv_heads * mb.head_dim * mb.kv_itemsize
+        pf_ms = mixed_part_ms(mb, pf_idx, mq, mkc, mvc, mt, ml, dev, stream)
+        dec_ms = mixed_part_ms(mb, dec_idx, mq, mkc, mvc, mt, ml, dev, stream)
         record["mixed_batch"] = {"workload": "mixed_chunked (256 seqs, 80% decode, lognormal chunks)",
                                  "num_tokens": mb.num_tokens, "out_dtype": "bf16", "ms": round(mixed_ms, 5),
                                  "tokens_per_s": round(mb.num_tokens / (mixed_ms * 1e-3), 1),
@@ -526,6 +560,14 @@ def main():
                                  "kv_gb": round(mb.kv_bytes() / 1e9, 4),
                                  # K/V once, queries once, outputs once: the batch's least HBM traffic
                                  "min_hbm_gb": round((mb.kv_bytes() + rows * 2 + rows * 2) / 1e9, 4),
+                                 "parts_alone": {
+                                     "prefill": {"seqs": int(len(pf_idx)), "ms": round(pf_ms, 5),
+                                                 "gflop": round(pf_flops / 1e9, 3),
+                                                 "mfma_util": round(pf_flops / (pf_ms * 1e-3) /
+                                                                    (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)},
+                                     "decode": {"seqs": int(len(dec_idx)), "ms": round(dec_ms, 5),
+                                                "kv_bytes": dec_kv,
+                                                "kv_gbs": round(dec_kv / (dec_ms * 1e-3) / 1e9, 1)}},
                                  "fp32_out": {"ms": round(times["fp32"], 5),
                                               "tokens_per_s": round(mb.num_tokens / (times["fp32"] * 1e-3), 1),
                                               "min_hbm_gb": round((mb.kv_bytes() + rows * 2 + rows * 4) / 1e9, 4)}}
