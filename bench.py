@@ -198,6 +198,7 @@ def cpu_baseline(bt, seconds):
                     break
     el = time.perf_counter() - t0
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"{n_seq} sequence decodes ({n_seq / bt.num_seqs:.2f} passes over the {bt.num_seqs}-sequence "
                       f"batch), numpy fp64 with BLAS limited to 1 thread, {el:.1f} s"}
 
