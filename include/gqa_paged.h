@@ -106,9 +106,10 @@ int32_t gqa_version(void);
  * chunks), each 16-position run of a value page's channel row is rewritten
  * whole around the new tokens (its other slots with the values they hold), so
  * a page that receives one sequence's new tokens must not receive another
- * sequence's in the same call (a paged allocator never does that).  ("[Performance] Use optimized kernels for MQA/GQA", opening
- * post: incoming keys/values are [tokens, num_kv_heads, head]; item 2: the
- * decode reads them back from a paged cache.)
+ * sequence's in the same call (a paged allocator never does that).
+ * ("[Performance] Use optimized kernels for MQA/GQA", opening post: incoming
+ * keys/values are [tokens, num_kv_heads, head]; item 2: the decode reads them
+ * back from a paged cache.)
  */
 int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                           const int32_t* block_tables, const int32_t* seq_lens,
@@ -175,9 +176,8 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
  * the pages.  The other decompositions run the cache write, then the decode.
  * Precondition of the balanced path (as in any paged allocator): the page
  * that receives a sequence's new token holds no other sequence's new token.
- * The caches end bit-identical to
- * reshape_and_cache's; the output agrees with reshape_and_cache followed by
- * paged_gqa_decode up to fp32 rounding.  seq_lens[b] == 0: nothing is written
+ * The caches end bit-identical to reshape_and_cache's; the output agrees with
+ * reshape_and_cache followed by paged_gqa_decode up to fp32 rounding.  seq_lens[b] == 0: nothing is written
  * and the output row is zero.  Errors as paged_gqa_decode, plus
  * GQA_ERR_INVALID_ARG for a null key or value.
  */
