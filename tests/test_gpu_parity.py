@@ -428,30 +428,43 @@ def check_rows(out, ref, rows, dtype, what):
     assert_parity(out[rows], ref[rows], dtype, what)
 
 
-def test_full_llama31_decode_sampled():
+@pytest.mark.parametrize("partition", [0, 512])
+def test_full_llama31_decode_sampled(partition):
+    """partition 0: the library's split (balanced at this shape), what the benchmark times."""
     bt = wl.llama31_8b_decode(seed=2)
     seqs = sampled(bt, 6, 0)
-    out = decode_step(bt, 512)
+    out = decode_step(bt, partition)
     check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
 
 
+@pytest.mark.parametrize("partition", [0, 256])
 @pytest.mark.parametrize("hkv", [32, 8, 1])
-def test_full_llama2_sweep_sampled(hkv):
+def test_full_llama2_sweep_sampled(hkv, partition):
     bt = wl.llama2_7b_sweep(hkv, seed=3)
     seqs = sampled(bt, 5, hkv)
-    out = decode_step(bt, 256)
+    out = decode_step(bt, partition)
     check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
 
 
-def test_full_mixed_sampled():
+@pytest.mark.parametrize("partition", [0, 512])
+def test_full_mixed_sampled(partition):
+    """partition 0: the library's decode split, what the benchmark times (with
+    bf16 output there: every element the fp32 result rounded to nearest even)."""
     bt = wl.mixed_chunked(seed=4)
     seqs = sampled(bt, 8, 4)
     big = int(np.argmax(bt.query_lens))
     seqs = sorted(set(seqs) | {big})
-    out = mixed_step(bt, 512)
+    d = DeviceBatch(bt)
+    d.cache_write()
+    o32 = d.mixed(partition)
+    out = host(o32)
     ref = oracle_after_write(bt, seqs=seqs, mixed=True)
     rows = np.concatenate([np.arange(bt.query_start_loc[b], bt.query_start_loc[b + 1]) for b in seqs])
     check_rows(out, ref, rows, bt.dtype, bt.describe())
+    if partition == 0:
+        o16 = d.mixed(partition, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(o32.to(torch.bfloat16), o16)
 
 
 @pytest.mark.parametrize("name", ["mixed", "decode"])
@@ -469,8 +482,10 @@ def test_full_cache_write_bit_exact(name):
     assert np.array_equal(ops.to_host_storage(dev.value_cache).view(np.uint8), vc.view(np.uint8))
 
 
-def test_full_longctx_splitk_sampled():
+@pytest.mark.parametrize("partition", [wl.LONGCTX_PARTITION, 0])
+def test_full_longctx_splitk_sampled(partition):
+    """Both splits the benchmark times: 512-token partitions and the library's."""
     bt = wl.longctx_splitk(seed=5)
     seqs = [0, 7, 15]
-    out = decode_step(bt, wl.LONGCTX_PARTITION)
+    out = decode_step(bt, partition)
     check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
