@@ -1,6 +1,6 @@
 """Reproducibility and HIP-graph capture of the attention calls.
 
-Every call is bitwise deterministic (no atomics in the arithmetic; merges
+Every call (the fused decode-and-append too) is bitwise deterministic (no atomics in the arithmetic; merges
 run in a fixed order), so two runs on the same inputs agree bit for bit.
 The library allocates nothing and never synchronises, so a serving loop can
 capture its calls in a HIP graph (torch.cuda.graph on ROCm) and replay them;
@@ -38,6 +38,15 @@ def calls():
                     lambda o, w, d=d, bt=bt, P=P: ops.paged_gqa_decode(
                         d.query, d.key_cache, d.value_cache, d.block_tables, d.seq_lens, bt.max_seq_len, bt.scale,
                         partition_size=P, out=o, workspace=w)))
+    # the fused append writes each sequence's new token into its slot; a repeated
+    # call writes the same bytes again, so every replay must give the same output
+    for P in (0, 256):
+        da = DeviceBatch(bt)
+        n = ops.decode_workspace_size(dims_of(bt, da), bt.max_seq_len, P)
+        out.append((f"append_P{P}", (bt.num_seqs, bt.num_heads, bt.head_dim), n,
+                    lambda o, w, d=da, bt=bt, P=P: ops.paged_gqa_decode_append(
+                        d.query, d.new_key, d.new_value, d.key_cache, d.value_cache, d.block_tables, d.seq_lens,
+                        bt.max_seq_len, bt.scale, partition_size=P, out=o, workspace=w)))
     mb = wl.mixed_chunked(seed=13, num_seqs=40, token_budget=1500)
     dm = DeviceBatch(mb)
     n = ops.mixed_workspace_size(dims_of(mb, dm), mb.num_tokens, mb.max_seq_len, 0)
@@ -64,16 +73,18 @@ def calls():
 
 
 CALLS = None
+N_CALLS = 7
 
 
 def get_calls():
     global CALLS
     if CALLS is None:
         CALLS = calls()
+        assert len(CALLS) == N_CALLS
     return CALLS
 
 
-@pytest.mark.parametrize("idx", range(5))
+@pytest.mark.parametrize("idx", range(N_CALLS))
 def test_bitwise_deterministic(idx):
     name, shape, nbytes, f = get_calls()[idx]
     ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
@@ -86,7 +97,7 @@ def test_bitwise_deterministic(idx):
     assert torch.equal(a, b), name
 
 
-@pytest.mark.parametrize("idx", range(5))
+@pytest.mark.parametrize("idx", range(N_CALLS))
 def test_graph_capture_replays_match_eager(idx):
     name, shape, nbytes, f = get_calls()[idx]
     ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
