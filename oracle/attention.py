@@ -121,10 +121,10 @@ def paged_attention_ref(query, key_cache, value_cache, block_tables, seq_lens, q
         for kv in range(num_kv_heads):
             K, V = gather_sequence(key_cache, value_cache, block_tables[b], L, kv)
             Qg = Q[q0:q1, kv * G:(kv + 1) * G, :]                                     # [q_len, G, d]
-            S = scale * np.einsum("jgd,td->jgt", Qg, K)
+            S = scale * np.matmul(Qg, K.T)                                            # [q_len, G, L]
             S = np.where(visible[:, None, :], S, -np.inf)
             W = _softmax_rows(S)
-            out[q0:q1, kv * G:(kv + 1) * G, :] = np.einsum("jgt,td->jgd", W, V)
+            out[q0:q1, kv * G:(kv + 1) * G, :] = np.matmul(W, V)
             if return_weights:
                 W_b[:, kv * G:(kv + 1) * G, :] = W
         if return_weights:
