@@ -1,8 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
 
-Small cases compare every output element; full-size workloads (the shapes and
-launch configuration the benchmark times) compare sampled sequences that the
-oracle computes one by one.  The bar: max-abs <= 1e-2 and relative L2 <= 2e-3
+Every test compares the whole output tensor: small cases, edge cases, and the
+full-size workloads in the launch configurations the benchmark times.  The bar: max-abs <= 1e-2 and relative L2 <= 2e-3
 for bf16 inputs with fp32 accumulation; fp32 inputs also meet relative L2 <=
 1e-5; the cache write is bit-exact.
 """
@@ -13,6 +12,7 @@ import torch
 from gqa_paged_kv_attention_amd import ops
 from gqa_paged_kv_attention_amd import workloads as wl
 from oracle import cache_write_ref, decode_ref, lse_merge_ref, paged_attention_ref
+from tests import full_size
 from tests.gpu_util import DeviceBatch, assert_parity, have_gpu, host, poison_tails
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -131,6 +131,24 @@ def test_decode_edge_shapes(dtype, d, hq, hkv):
         out = host(dev.decode(partition))
         assert_parity(out, ref, dtype, f"{bt.describe()} P={partition}")
         assert np.all(out[0] == 0)          # empty sequence -> zero row
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_g32_round_robin_schedule(d):
+    """bf16 with G = 32 (two row blocks per wave): the four waves of a work-group
+    take a partition's 32-token tiles round-robin through the alternating
+    double-buffered schedule (stride 4, clamped prefetches past the last
+    tile).  Every length from 1 to 300 tokens, so each wave's first and last
+    tile positions, and partitions with fewer tiles than waves, all occur;
+    unsplit and in 64- and 160-token partitions."""
+    lens = np.arange(1, 301)
+    bt = wl.make_batch(name="g32", seed=d + 32, num_heads=32, num_kv_heads=1, head_dim=d, block_size=16,
+                       seq_lens=lens, query_lens=np.ones(len(lens), np.int64), dtype=wl.BF16, poison_slack=True)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, 1, bt.scale)
+    for partition in (0, 64, 160):
+        assert_parity(host(dev.decode(partition)), ref, wl.BF16, f"{bt.describe()} P={partition}")
 
 
 def test_decode_peaky_scores_exercise_rescale():
@@ -411,60 +429,56 @@ def test_prefill_chunk_invariance_on_gpu():
     assert np.max(np.abs(np.concatenate(parts) - whole)) <= 1e-5
 
 
+@pytest.mark.parametrize("v_scale", [1e-4, 1e-5])
+def test_mixed_small_values(v_scale):
+    """Values far below 1 (N(0, s^2) with s = 1e-4, 1e-5): the prefill rows
+    convert V to fp16, where magnitudes under 2^-14 become subnormals; the
+    conversion rounds to nearest, so the error stays unbiased and the whole
+    output meets the bar (a CPU model of the conversion puts its share of the
+    relative L2 error at 5e-5 and 1.4e-3)."""
+    bt = wl.mixed_chunked(seed=41, num_seqs=24, token_budget=900)
+    for arr in (bt.value_cache, bt.new_value):
+        scaled = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(arr) * np.float32(v_scale))
+        arr[...] = scaled
+    out = mixed_step(bt, 0)
+    assert_parity(out, oracle_after_write(bt, mixed=True), bt.dtype, f"{bt.describe()} V x {v_scale:g}")
+
+
 # --------------------------------------------------------------------------
-# full-size workloads, sampled sequences (benchmark launch configuration)
+# full-size workloads: the whole output against the oracle, in the launch
+# configurations the benchmark times
 # --------------------------------------------------------------------------
-
-def sampled(bt, k, seed):
-    rng = np.random.default_rng(seed)
-    order = np.argsort(bt.seq_lens)
-    picks = {int(order[0]), int(order[-1])}
-    picks |= set(int(x) for x in rng.choice(bt.num_seqs, size=min(k, bt.num_seqs), replace=False))
-    return sorted(picks)
-
-
-def check_rows(out, ref, rows, dtype, what):
-    assert np.isfinite(out).all(), what
-    assert_parity(out[rows], ref[rows], dtype, what)
-
 
 @pytest.mark.parametrize("partition", [0, 512])
-def test_full_llama31_decode_sampled(partition):
+def test_full_llama31_decode(partition):
     """partition 0: the library's split (balanced at this shape), what the benchmark times."""
     bt = wl.llama31_8b_decode(seed=2)
-    seqs = sampled(bt, 6, 0)
-    out = decode_step(bt, partition)
-    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
+    assert_parity(decode_step(bt, partition), full_size.llama31_decode(), bt.dtype, bt.describe())
 
 
 @pytest.mark.parametrize("partition", [0, 256])
 @pytest.mark.parametrize("hkv", [32, 8, 1])
-def test_full_llama2_sweep_sampled(hkv, partition):
+def test_full_llama2_sweep(hkv, partition):
     bt = wl.llama2_7b_sweep(hkv, seed=3)
-    seqs = sampled(bt, 5, hkv)
-    out = decode_step(bt, partition)
-    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
+    assert_parity(decode_step(bt, partition), full_size.llama2_sweep(hkv), bt.dtype, bt.describe())
 
 
 @pytest.mark.parametrize("partition", [0, 512])
-def test_full_mixed_sampled(partition):
+def test_full_mixed(partition):
     """partition 0: the library's decode split, what the benchmark times (with
-    bf16 output there: every element the fp32 result rounded to nearest even)."""
+    bf16 output there: every element the fp32 result rounded to nearest even,
+    and the bf16 output itself within the bar)."""
     bt = wl.mixed_chunked(seed=4)
-    seqs = sampled(bt, 8, 4)
-    big = int(np.argmax(bt.query_lens))
-    seqs = sorted(set(seqs) | {big})
     d = DeviceBatch(bt)
     d.cache_write()
     o32 = d.mixed(partition)
-    out = host(o32)
-    ref = oracle_after_write(bt, seqs=seqs, mixed=True)
-    rows = np.concatenate([np.arange(bt.query_start_loc[b], bt.query_start_loc[b + 1]) for b in seqs])
-    check_rows(out, ref, rows, bt.dtype, bt.describe())
+    ref = full_size.mixed()
+    assert_parity(host(o32), ref, bt.dtype, bt.describe())
     if partition == 0:
         o16 = d.mixed(partition, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         assert torch.equal(o32.to(torch.bfloat16), o16)
+        assert np.max(np.abs(host(o16) - ref)) <= 1e-2
 
 
 @pytest.mark.parametrize("name", ["mixed", "decode"])
@@ -483,9 +497,7 @@ def test_full_cache_write_bit_exact(name):
 
 
 @pytest.mark.parametrize("partition", [wl.LONGCTX_PARTITION, 0])
-def test_full_longctx_splitk_sampled(partition):
+def test_full_longctx_splitk(partition):
     """Both splits the benchmark times: 512-token partitions and the library's."""
     bt = wl.longctx_splitk(seed=5)
-    seqs = [0, 7, 15]
-    out = decode_step(bt, partition)
-    check_rows(out, oracle_after_write(bt, seqs=seqs), seqs, bt.dtype, bt.describe())
+    assert_parity(decode_step(bt, partition), full_size.longctx(), bt.dtype, bt.describe())
