@@ -74,15 +74,20 @@ void shared_prefix_kernel(SharedPrefixArgs a) {
   const int p = u % nparts, b = u / nparts;
   const int L = clamp_len(a.decode.seq_lens[b], a.decode.max_blocks_per_seq, BS);
   // group of sequence b: the one whose [group_start[t], group_start[t + 1]) holds b
+  // (chunks of kThreads groups; every thread reads the result into a register
+  // before the barrier that lets any thread write the next chunk's, so all
+  // threads leave the loop after the same chunk)
   if (threadIdx.x == 0) s_group = -1;
   __syncthreads();
+  int g = -1;
   for (int t0 = 0; t0 < a.num_groups; t0 += kThreads) {
     const int t = t0 + threadIdx.x;
     if (t < a.num_groups && a.group_start[t] <= b && b < a.group_start[t + 1]) s_group = t;
     __syncthreads();
-    if (s_group >= 0) break;
+    g = s_group;
+    __syncthreads();
+    if (g >= 0) break;
   }
-  const int g = s_group;
   const int shared = g >= 0 ? shared_keys<BS>(a, a.prefix_lens[g]) : 0;
   const int rest = min(L, shared + nparts * a.decode.partition_size) - shared;
   const int n_sp = rest > 0 ? (rest + a.decode.partition_size - 1) / a.decode.partition_size : 0;
@@ -145,15 +150,13 @@ hipError_t dispatch(const SharedPrefixArgs& a, hipStream_t s) {
   const long long groups = (long long)a.num_groups * a.row_tiles * a.prefix_chunks * a.prefill.num_kv_heads +
                            (long long)a.num_seqs * a.decode.max_partitions * a.prefill.num_kv_heads;
   if (groups > 0) {
-    if (a.prefill.group <= 16)
-      hipLaunchKernelGGL((shared_prefix_kernel<D, 1, BS, OutT>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((shared_prefix_kernel<D, 2, BS, OutT>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    const hipError_t e =
+        a.prefill.group <= 16
+            ? launch_kernel(shared_prefix_kernel<D, 1, BS, OutT>, dim3((unsigned)groups), dim3(kThreads), 0, s, a)
+            : launch_kernel(shared_prefix_kernel<D, 2, BS, OutT>, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((shared_prefix_merge_kernel<D, OutT>), dim3(a.prefill.num_heads, a.num_seqs), dim3(D), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(shared_prefix_merge_kernel<D, OutT>, dim3(a.prefill.num_heads, a.num_seqs), dim3(D), 0, s, a);
 }
 
 }  // namespace

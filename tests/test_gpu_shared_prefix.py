@@ -12,6 +12,7 @@ import torch
 from gqa_paged_kv_attention_amd import ops
 from gqa_paged_kv_attention_amd import workloads as wl
 from oracle import decode_ref
+from tests import full_size
 from tests.gpu_util import DeviceBatch, assert_parity, have_gpu, host, poison_tails
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -99,6 +100,21 @@ def test_shared_prefix_fp32_runs_plain_decode():
     assert_parity(host(out), oracle(bt), bt.dtype, bt.describe())
 
 
+def test_shared_prefix_many_groups():
+    """More groups than a work-group has threads (300 groups of one or two
+    members, prefixes on and off 64-key tiles): the suffix units find their
+    sequence's group in a later chunk of the group list."""
+    rng = np.random.default_rng(31)
+    groups = []
+    for g in range(300):
+        members = 1 + g % 2
+        groups.append((members, 16 * int(rng.integers(0, 9)), [int(x) for x in rng.integers(1, 90, members)]))
+    bt, starts, prefixes = grouped_batch(30, groups, hq=8, hkv=2, d=64)
+    for partition in (0, 64):
+        _, out = run_shared(bt, starts, prefixes, partition=partition)
+        assert_parity(host(out), oracle(bt), bt.dtype, f"{bt.describe()} P={partition}")
+
+
 def test_shared_prefix_workspace_reuse():
     """One workspace, two calls in a row (the second smaller): each call
     rewrites the partial counts it reads."""
@@ -118,14 +134,10 @@ def test_shared_prefix_workspace_reuse():
 
 
 @pytest.mark.parametrize("prefix_len,group_size", [(2048, 16), (4096, 64)])
-def test_full_shared_prefix_sampled(prefix_len, group_size):
-    """Benchmark shapes: groups sharing a long prompt, sampled sequences."""
+def test_full_shared_prefix(prefix_len, group_size):
+    """Benchmark shapes: groups sharing a long prompt; the whole output against
+    the oracle's plain decode of every sequence."""
     bt, starts, prefixes = wl.shared_prefix_decode(seed=7, num_groups=4, group_size=group_size,
                                                    prefix_len=prefix_len)
     _, out = run_shared(bt, starts, prefixes)
-    out = host(out)
-    assert np.isfinite(out).all()
-    seqs = sorted({0, 1, group_size - 1, group_size, 3 * group_size + 5, bt.num_seqs - 1})
-    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, bt.num_kv_heads,
-                     bt.scale, seqs=seqs)
-    assert_parity(out[seqs], ref[seqs], bt.dtype, bt.describe())
+    assert_parity(host(out), full_size.shared_prefix(prefix_len, group_size), bt.dtype, bt.describe())
