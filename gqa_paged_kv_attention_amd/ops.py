@@ -129,6 +129,42 @@ def _check_int32(*ts):
             raise TypeError("block tables, lengths and index arrays must be int32")
 
 
+def _shape_error(what: str, got, want):
+    raise ValueError(f"{what} has shape {tuple(got)}, expected {tuple(want)}")
+
+
+def _check_caches(key_cache, value_cache):
+    """key_cache [num_blocks, Hkv, bs, d] (token-major pages), value_cache
+    [num_blocks, Hkv, d, bs] (channel-major pages); returns (nb, Hkv, bs, d)."""
+    if key_cache.dim() != 4:
+        _shape_error("key_cache", key_cache.shape, ("num_blocks", "Hkv", "block_size", "head_dim"))
+    nb, hkv, bs, d = key_cache.shape
+    if tuple(value_cache.shape) != (nb, hkv, d, bs):
+        _shape_error("value_cache", value_cache.shape, (nb, hkv, d, bs))
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache must share a dtype")
+    return nb, hkv, bs, d
+
+
+def _check_rows(name, t, rows, hq, d):
+    if t is not None and tuple(t.shape) != (rows, hq, d):
+        _shape_error(name, t.shape, (rows, hq, d))
+
+
+def _check_tables(block_tables, num_seqs, seq_lens, query_start_loc=None, lens_name="seq_lens"):
+    if block_tables.dim() != 2 or block_tables.shape[0] < num_seqs or block_tables.shape[1] < 1:
+        _shape_error("block_tables", block_tables.shape, (f">={num_seqs}", "max_blocks_per_seq"))
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != num_seqs:
+        _shape_error(lens_name, seq_lens.shape, (num_seqs,))
+    if query_start_loc is not None and (query_start_loc.dim() != 1 or query_start_loc.shape[0] != num_seqs + 1):
+        _shape_error("query_start_loc", query_start_loc.shape, (num_seqs + 1,))
+
+
+def _check_query(query, hkv, d):
+    if query.dim() != 3 or query.shape[2] != d or query.shape[1] % hkv != 0:
+        _shape_error("query", query.shape, ("tokens", f"a multiple of {hkv}", d))
+
+
 def make_dims(*, num_seqs, num_heads, key_cache, block_tables, q_dtype, out_dtype) -> Dims:
     nb, hkv, bs, d = key_cache.shape
     return Dims(num_seqs, num_heads, hkv, d, bs, nb, block_tables.shape[1], _dtype_code(q_dtype),
@@ -147,6 +183,12 @@ def _call(fn: str, status: int):
 
 def reshape_and_cache(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc, stream=None):
     """Write new keys/values ``[T, Hkv, d]`` into the paged caches (in place)."""
+    nb, hkv, bs, d = _check_caches(key_cache, value_cache)
+    if key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        _shape_error("key", key.shape, ("tokens", hkv, d))
+    if tuple(value.shape) != tuple(key.shape):
+        _shape_error("value", value.shape, key.shape)
+    _check_tables(block_tables, seq_lens.shape[0] if seq_lens.dim() == 1 else -1, seq_lens, query_start_loc)
     lib = load_library()
     _check_device(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc)
     _check_int32(block_tables, seq_lens, query_start_loc)
@@ -181,10 +223,14 @@ def _workspace(nbytes: int, device, workspace):
 def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
                      partition_size: int = 0, out=None, out_dtype=None, workspace=None, stream=None):
     """Decode attention: ``query [B, Hq, d]`` -> ``out [B, Hq, d]``."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    B, Hq, d = query.shape
+    _check_rows("out", out, B, Hq, d)
+    _check_tables(block_tables, B, seq_lens)
     lib = load_library()
     _check_device(query, key_cache, value_cache, block_tables, seq_lens, out, workspace)
     _check_int32(block_tables, seq_lens)
-    B, Hq, d = query.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
@@ -205,10 +251,16 @@ def paged_gqa_decode_append(query, key, value, key_cache, value_cache, block_tab
     """One decode step with the cache write fused: ``key``/``value [B, Hkv, d]`` (each sequence's new
     token, at position seq_lens[b] - 1) go into the caches, and ``query [B, Hq, d]`` -> ``out [B, Hq, d]``
     attends over all seq_lens[b] tokens."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    B, Hq, d = query.shape
+    _check_rows("out", out, B, Hq, d)
+    _check_rows("key", key, B, hkv, d)
+    _check_rows("value", value, B, hkv, d)
+    _check_tables(block_tables, B, seq_lens)
     lib = load_library()
     _check_device(query, key, value, key_cache, value_cache, block_tables, seq_lens, out, workspace)
     _check_int32(block_tables, seq_lens)
-    B, Hq, d = query.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
@@ -227,12 +279,26 @@ def splitk_lse_reduce(partial_out, partial_lse, seq_lens, partition_size: int, *
                       block_size: int = 16, max_blocks_per_seq: int, query_start_loc=None, out=None,
                       out_dtype=None, skip_single: bool = False, num_out_rows: Optional[int] = None, stream=None):
     """Merge split-K partials ``[B, Hq, P, d]`` / ``[B, Hq, P]`` into ``out``."""
+    if partial_out.dim() != 4:
+        _shape_error("partial_out", partial_out.shape, ("num_seqs", "Hq", "partitions", "head_dim"))
+    B, Hq, P, d = partial_out.shape
+    if tuple(partial_lse.shape) != (B, Hq, P):
+        _shape_error("partial_lse", partial_lse.shape, (B, Hq, P))
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        _shape_error("seq_lens", seq_lens.shape, (B,))
+    if query_start_loc is not None and (query_start_loc.dim() != 1 or query_start_loc.shape[0] != B + 1):
+        _shape_error("query_start_loc", query_start_loc.shape, (B + 1,))
+    if Hq % num_kv_heads != 0:
+        raise ValueError(f"num_kv_heads {num_kv_heads} does not divide {Hq} heads")
+    if out is not None:
+        rows = query_start_loc is not None
+        if out.dim() != 3 or tuple(out.shape[1:]) != (Hq, d) or (not rows and out.shape[0] != B):
+            _shape_error("out", out.shape, ("rows" if rows else B, Hq, d))
     lib = load_library()
     _check_device(partial_out, partial_lse, seq_lens, query_start_loc, out)
     _check_int32(seq_lens, query_start_loc)
     if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
         raise TypeError("partials are float32")
-    B, Hq, P, d = partial_out.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         rows = num_out_rows if num_out_rows is not None else B
@@ -249,10 +315,14 @@ def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, se
                                  max_query_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
                                  out=None, out_dtype=None, workspace=None, stream=None):
     """Mixed prefill-chunk + decode attention: ``query [T, Hq, d]`` -> ``out [T, Hq, d]``."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    T, Hq, d = query.shape
+    _check_rows("out", out, T, Hq, d)
+    _check_tables(block_tables, seq_lens.shape[0] if seq_lens.dim() == 1 else -1, seq_lens, query_start_loc)
     lib = load_library()
     _check_device(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, out, workspace)
     _check_int32(block_tables, seq_lens, query_start_loc)
-    T, Hq, d = query.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         out = torch.empty(T, Hq, d, dtype=out_dtype, device=query.device)
@@ -277,10 +347,15 @@ def paged_cross_attention(query, key_cache, value_cache, block_tables, encoder_l
                           max_query_len: int, max_encoder_len: int, scale: float, partition_size: int = 0,
                           out=None, out_dtype=None, workspace=None, stream=None):
     """Cross-attention of decoder rows ``query [T, Hq, d]`` over a static encoder cache -> ``out [T, Hq, d]``."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    T, Hq, d = query.shape
+    _check_rows("out", out, T, Hq, d)
+    _check_tables(block_tables, encoder_lens.shape[0] if encoder_lens.dim() == 1 else -1, encoder_lens,
+                  query_start_loc, lens_name="encoder_lens")
     lib = load_library()
     _check_device(query, key_cache, value_cache, block_tables, encoder_lens, query_start_loc, out, workspace)
     _check_int32(block_tables, encoder_lens, query_start_loc)
-    T, Hq, d = query.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         out = torch.empty(T, Hq, d, dtype=out_dtype, device=query.device)
@@ -307,10 +382,16 @@ def paged_gqa_decode_shared_prefix(query, key_cache, value_cache, block_tables, 
                                    out=None, out_dtype=None, workspace=None, stream=None):
     """Decode ``query [B, Hq, d]`` -> ``out [B, Hq, d]`` where the sequences of group g
     (``group_start[g] .. group_start[g+1]-1``) share their first ``prefix_lens[g]`` tokens."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    B, Hq, d = query.shape
+    _check_rows("out", out, B, Hq, d)
+    _check_tables(block_tables, B, seq_lens)
+    if prefix_lens.dim() != 1 or group_start.dim() != 1 or group_start.shape[0] != prefix_lens.shape[0] + 1:
+        _shape_error("group_start", group_start.shape, (prefix_lens.shape[0] + 1,))
     lib = load_library()
     _check_device(query, key_cache, value_cache, block_tables, seq_lens, group_start, prefix_lens, out, workspace)
     _check_int32(block_tables, seq_lens, group_start, prefix_lens)
-    B, Hq, d = query.shape
     out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
     if out is None:
         out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
