@@ -11,6 +11,7 @@
 
 #include "gqa_common.h"
 #include "gqa_internal.h"
+#include "tile_schedule.h"
 
 namespace gqa {
 
@@ -108,10 +109,6 @@ struct TilePages {
   }
 };
 
-// A wave that walks consecutive tiles loads them in pairs (see run_tiles).
-template <class Tile>
-constexpr bool kPairedTiles = Tile::kPipelined;
-
 template <class Tile, int D>
 __device__ __forceinline__ void load_tile(typename Tile::K& kf, typename Tile::V& vf, const TilePages<Tile, D>& pg,
                                           const void* kc, const void* vc, int num_kv_heads, int kv, int lane) {
@@ -150,14 +147,19 @@ __device__ __forceinline__ void compute_tile(WaveState<Tile, NT>& st, const type
 // past L are zeroed so that whatever sits in the pool beyond the sequence
 // (including NaN) cannot reach the output.
 //
-// Two register sets (A, B).  A wave that walks consecutive tiles (step 1)
-// loads them in pairs, then computes both.  Otherwise (tiles shared round-
-// robin by the waves of a work-group) the sets alternate: the loads of the
-// next tile are issued before the current tile is computed, so a wave always
-// has a tile in flight.  Prefetches are unconditional (the tile index is
-// clamped to the last tile, whose re-read hits in cache), which keeps the load
-// count per iteration fixed and lets the compiler wait on just the tile about
-// to be computed.
+// The visiting order is tile_schedule's (tile_schedule.h, checked on the host
+// for every range a work-group produces).  Pipelined tiles use two register
+// sets (A, B): a wave that walks consecutive tiles (step 1) loads them in
+// pairs, then computes both, so it has 64 tokens of K and V in flight at once
+// (with 64-token pages the pair is one page and the two halves of every value
+// line are requested together; one tile at a time, L2 evicted most lines
+// before the second half was asked for: +34% HBM reads).  Otherwise (tiles
+// shared round-robin by the waves of a work-group) the sets alternate: the
+// loads of the next tile are issued before the current tile is computed.
+// Prefetches past the last tile repeat it (its re-read hits in cache), which
+// keeps the load count per round fixed and lets the compiler wait on just the
+// tile about to be computed.  Register and page-set indices are literals at
+// every call of the callbacks, so the selects below fold away.
 template <class Tile, int D, int NT>
 __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typename Tile::Q qf[NT], const void* kc,
                                           const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
@@ -165,59 +167,19 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
   if (it0 >= it1) return;
   // at least one page: a fused append walks the tile of its only key with L = 0
   const int npages = max(1, (L + Tile::kBS - 1) / Tile::kBS);
-  if constexpr (!Tile::kPipelined) {
-    for (int it = it0; it < it1; it += step) {
-      typename Tile::K kf;
-      typename Tile::V vf;
-      TilePages<Tile, D> pg;
-      pg.fetch(bt, it, npages, num_blocks);
-      load_tile<Tile, D>(kf, vf, pg, kc, vc, num_kv_heads, kv, lane);
-      compute_tile<Tile, NT>(st, qf, kf, vf, it * kTile, L, lim, scale_log2, lane);
-    }
-    return;
-  }
-  const int last = it0 + (it1 - 1 - it0) / step * step;     // last tile this wave visits
   typename Tile::K kA, kB;
   typename Tile::V vA, vB;
-  if constexpr (kPairedTiles<Tile>) {
-    if (step == 1) {
-      // Tiles in pairs: both tiles' loads are issued together, then both are
-      // computed, so a wave has 64 tokens of K and V in flight at once.  With
-      // 64-token pages the pair is one page and the two halves of every value
-      // line are requested together (one tile at a time, L2 evicted most lines
-      // before the second half was asked for: +34% HBM reads).  The page ids
-      // of the next pair are loaded while this pair is computed; a pair past
-      // the end repeats the last tile, whose result is not used.
-      TilePages<Tile, D> pa, pb;
-      pa.fetch(bt, it0, npages, num_blocks);
-      pb.fetch(bt, min(it0 + 1, last), npages, num_blocks);
-      for (int it = it0; it < it1; it += 2) {
-        load_tile<Tile, D>(kA, vA, pa, kc, vc, num_kv_heads, kv, lane);
-        load_tile<Tile, D>(kB, vB, pb, kc, vc, num_kv_heads, kv, lane);
-        pa.fetch(bt, min(it + 2, last), npages, num_blocks);
-        pb.fetch(bt, min(it + 3, last), npages, num_blocks);
-        compute_tile<Tile, NT>(st, qf, kA, vA, it * kTile, L, lim, scale_log2, lane);
-        if (it + 1 < it1) compute_tile<Tile, NT>(st, qf, kB, vB, (it + 1) * kTile, L, lim, scale_log2, lane);
-      }
-      return;
-    }
-  }
-  TilePages<Tile, D> pg;
-  pg.fetch(bt, it0, npages, num_blocks);
-  load_tile<Tile, D>(kA, vA, pg, kc, vc, num_kv_heads, kv, lane);
-  pg.fetch(bt, min(it0 + step, last), npages, num_blocks);
-  for (int it = it0;; it += 2 * step) {
-    // B <- tile it + step (clamped), then compute A = tile it
-    load_tile<Tile, D>(kB, vB, pg, kc, vc, num_kv_heads, kv, lane);
-    pg.fetch(bt, min(it + 2 * step, last), npages, num_blocks);
-    compute_tile<Tile, NT>(st, qf, kA, vA, it * kTile, L, lim, scale_log2, lane);
-    if (it + step > last) break;
-    // A <- tile it + 2 step (clamped), then compute B = tile it + step
-    load_tile<Tile, D>(kA, vA, pg, kc, vc, num_kv_heads, kv, lane);
-    pg.fetch(bt, min(it + 3 * step, last), npages, num_blocks);
-    compute_tile<Tile, NT>(st, qf, kB, vB, (it + step) * kTile, L, lim, scale_log2, lane);
-    if (it + 2 * step > last) break;
-  }
+  TilePages<Tile, D> pa, pb;
+  auto fetch = [&](int p, int tile) __attribute__((always_inline)) {
+    (p == 0 ? pa : pb).fetch(bt, tile, npages, num_blocks);
+  };
+  auto load = [&](int r, int p) __attribute__((always_inline)) {
+    load_tile<Tile, D>(r == 0 ? kA : kB, r == 0 ? vA : vB, p == 0 ? pa : pb, kc, vc, num_kv_heads, kv, lane);
+  };
+  auto compute = [&](int r, int tile) __attribute__((always_inline)) {
+    compute_tile<Tile, NT>(st, qf, r == 0 ? kA : kB, r == 0 ? vA : vB, tile * kTile, L, lim, scale_log2, lane);
+  };
+  tile_schedule(it0, it1, step, Tile::kPipelined ? kPaired : kSingle, fetch, load, compute);
 }
 
 // Clamp a sequence length into what the block table can address.
