@@ -3,6 +3,10 @@
 // for prefill, the chunk's new tokens times G) form the 16-wide column block of
 // the matrix-core products described in gqa_common.h; the per-wave tile
 // pipeline is in decode_core.h.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "decode_core.h"
 
 namespace gqa {
@@ -341,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   __shared__ int s_scan[kThreads];          // one entry per thread: locate_prefill_tile scans over them
   __shared__ int s_found[2];
+  static_assert(sizeof(s_scan) / sizeof(s_scan[0]) == kThreads, "the tile locator indexes s_scan by thread");
   int local = 0;
   const int b = locate_prefill_tile(a.query_start_loc, a.num_seqs, G, RWG, tile, s_scan, s_found, &local);
   if (b < 0) return;
@@ -426,11 +431,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 template <class Tile, int D, class OutT>
 hipError_t decode_dispatch_nt(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
   dim3 grid(a.max_partitions, a.num_kv_heads, num_seqs);
-  if (a.group <= 16)
-    hipLaunchKernelGGL((decode_kernel<Tile, D, 1, OutT>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<Tile, D, 2, OutT>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  if (a.group <= 16) return launch_kernel(decode_kernel<Tile, D, 1, OutT>, grid, dim3(kThreads), 0, stream, a);
+  return launch_kernel(decode_kernel<Tile, D, 2, OutT>, grid, dim3(kThreads), 0, stream, a);
 }
 
 // Call f(Tile type tag, head dim tag) for the cache dtype, head_dim and page size.
@@ -481,31 +483,46 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bo
     typedef decltype(tile) Tile;
     constexpr int DD = decltype(dd)::value;
     if (out_f32)
-      hipLaunchKernelGGL((prefill_kernel<Tile, DD, kPrefillNTW, float>), dim3(grid_groups), dim3(kThreads), 0,
+      return launch_kernel(prefill_kernel<Tile, DD, kPrefillNTW, float>, dim3(grid_groups), dim3(kThreads), 0,
+                           stream, a);
+    return launch_kernel(prefill_kernel<Tile, DD, kPrefillNTW, uint16_t>, dim3(grid_groups), dim3(kThreads), 0,
                          stream, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<Tile, DD, kPrefillNTW, uint16_t>), dim3(grid_groups), dim3(kThreads), 0,
-                         stream, a);
-    return hipGetLastError();
   });
 }
 
+// Workers of the balanced decode: compute units x resident work-groups per
+// compute unit x 4 waves.  The compute-unit count and the kernel's occupancy
+// are queried once per (device, kernel, 1 KiB step of its dynamic LDS) and
+// cached: workspace queries and decode calls then make no runtime query beyond
+// hipGetDevice.  The occupancy is taken at the top of the LDS step, so it never
+// exceeds what the launch's actual LDS allows.
 int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs) {
-  int dev = 0, cus = 256, per_cu = 2;
-  if (hipGetDevice(&dev) == hipSuccess) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const size_t lds_step = ((size_t)(2 * num_seqs + 1) * sizeof(int) + 1023) / 1024;
+  void (*kernel)(StreamArgs) =
+      with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [](void (*k)(StreamArgs)) { return k; });
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kernel), lds_step);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int cus = 256, per_cu = 2;
+  if (dev >= 0) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    const size_t lds = (size_t)(2 * num_seqs + 1) * sizeof(int);
-    with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [&](void (*k)(StreamArgs)) {
-      int blocks = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(k), kThreads, lds) ==
-              hipSuccess && blocks > 0)
-        per_cu = blocks;
-      return 0;
-    });
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(kernel), kThreads,
+                                                     lds_step * 1024) == hipSuccess && blocks > 0)
+      per_cu = blocks;
   }
-  (void)hipGetLastError();
-  return cus * per_cu * kWaves;
+  const int workers = cus * per_cu * kWaves;
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = workers;
+  return workers;
 }
 
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
@@ -513,27 +530,23 @@ hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_siz
   const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
   const dim3 grid(a.num_workers / kWaves), block(kThreads);
   return with_stream_kernel(head_dim, block_size, kv_f32, out_f32, a.group, [&](void (*k)(StreamArgs)) {
-    hipLaunchKernelGGL(k, grid, block, lds, stream, a);
-    return hipGetLastError();
+    return launch_kernel(k, grid, block, lds, stream, a);
   });
 }
 
 template <class InT>
-void reduce_dispatch(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream) {
+hipError_t reduce_dispatch(const StreamArgs& a, int head_dim, bool out_f32, hipStream_t stream) {
   const dim3 grid(a.num_kv_heads * a.num_seqs, a.group);
-  if (head_dim == 64) {
-    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<64, float, InT>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((stream_reduce_kernel<64, uint16_t, InT>), grid, dim3(64), 0, stream, a);
-  } else {
-    if (out_f32) hipLaunchKernelGGL((stream_reduce_kernel<128, float, InT>), grid, dim3(128), 0, stream, a);
-    else hipLaunchKernelGGL((stream_reduce_kernel<128, uint16_t, InT>), grid, dim3(128), 0, stream, a);
-  }
+  if (head_dim == 64)
+    return out_f32 ? launch_kernel(stream_reduce_kernel<64, float, InT>, grid, dim3(64), 0, stream, a)
+                   : launch_kernel(stream_reduce_kernel<64, uint16_t, InT>, grid, dim3(64), 0, stream, a);
+  return out_f32 ? launch_kernel(stream_reduce_kernel<128, float, InT>, grid, dim3(128), 0, stream, a)
+                 : launch_kernel(stream_reduce_kernel<128, uint16_t, InT>, grid, dim3(128), 0, stream, a);
 }
 
 hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream) {
-  if (kv_f32) reduce_dispatch<float>(a, head_dim, out_f32, stream);
-  else reduce_dispatch<uint16_t>(a, head_dim, out_f32, stream);
-  return hipGetLastError();
+  return kv_f32 ? reduce_dispatch<float>(a, head_dim, out_f32, stream)
+                : reduce_dispatch<uint16_t>(a, head_dim, out_f32, stream);
 }
 
 }  // namespace gqa

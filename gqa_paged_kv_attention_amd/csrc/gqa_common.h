@@ -78,15 +78,18 @@ __device__ __forceinline__ f32x4_t mfma_f16(uint4 a, uint4 b, f32x4_t c) {
                                                  0, 0, 0);
 }
 
-// Two bf16 (packed in a word) -> two fp16 (packed), rounding toward zero: exact
-// for values representable in fp16; larger magnitudes saturate at 65504.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x << 16),
-                                                                 __uint_as_float(x & 0xffff0000u)));
-}
-
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two bf16 (packed in a word) -> two fp16 (packed), round to nearest even (one
+// v_cvt_pk_f16_f32).  Exact for magnitudes in [2^-14, 65504] (a bf16
+// significand fits fp16's); smaller ones become fp16 subnormals (absolute
+// error <= 2^-25, unbiased), larger ones overflow to infinity.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                          (f32x2_t{__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u)}),
+                                          f16x2_t));
+}
 
 // Two fp32 -> two fp16 (packed), round to nearest even (one v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
@@ -363,11 +366,14 @@ struct TileF32 {
 // Locate this work-group's (sequence, row tile) among the row tiles of the
 // sequences with more than one query token (ceil(q_len * G / rows_per_group)
 // tiles each, in sequence order): a block-wide scan of the tile counts, in
-// chunks of blockDim.x sequences.  s_scan holds blockDim.x ints.  Returns the
-// sequence (or -1 past the last tile) and the tile's index within it.
+// chunks of NTHR sequences, one entry of s_scan per thread.  The work-group
+// must have exactly NTHR threads (the caller's launch bound), so that every
+// thread's entry exists.  Returns the sequence (or -1 past the last tile) and
+// the tile's index within it.
+template <int NTHR>
 __device__ __forceinline__ int locate_prefill_tile(const int32_t* qsl, int num_seqs, int G, int rows_per_group,
-                                                   int tile, int* s_scan, int* s_found, int* local_tile) {
-  const int nthr = blockDim.x;
+                                                   int tile, int (&s_scan)[NTHR], int* s_found, int* local_tile) {
+  constexpr int nthr = NTHR;
   if (threadIdx.x == 0) s_found[0] = -1;
   int base = 0;
   for (int c0 = 0; c0 < num_seqs; c0 += nthr) {

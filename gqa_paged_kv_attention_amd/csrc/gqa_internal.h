@@ -6,6 +6,16 @@
 
 namespace gqa {
 
+// Launch kernel k (whose one parameter is a struct passed by value) and return
+// the status of this launch alone.  hipLaunchKernel reports its own result, so
+// an error left pending by the caller's earlier HIP calls is neither read as
+// this launch's nor cleared.
+template <class Args>
+inline hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, size_t lds, hipStream_t s, const Args& a) {
+  void* args[] = {const_cast<Args*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, lds, s);
+}
+
 // Fixed-partition decode (one work-group per (partition, kv head, sequence)).
 struct DecodeArgs {
   void* out;

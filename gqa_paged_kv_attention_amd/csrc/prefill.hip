@@ -368,10 +368,9 @@ void mixed_kernel(MixedArgs a) {
 template <int D, int BS, class OutT>
 hipError_t mixed_dispatch(const MixedArgs& a, int groups, hipStream_t s) {
   if (a.prefill.group <= 16)
-    hipLaunchKernelGGL((mixed_kernel<D, 1, BS, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
+    return launch_kernel(mixed_kernel<D, 1, BS, OutT>, dim3(groups), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((mixed_kernel<D, 2, BS, OutT>), dim3(groups), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+    return launch_kernel(mixed_kernel<D, 2, BS, OutT>, dim3(groups), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
@@ -379,8 +378,7 @@ hipError_t mixed_dispatch(const MixedArgs& a, int groups, hipStream_t s) {
 int prefill_lds_rows_per_group() { return PrefillLds<128, kLdsNTW>::kRowsPerGroup; }
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
 }
 
 hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,

@@ -12,9 +12,12 @@
 // one is consumed) and each wave multiplies it against its own rows:
 //   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 out),
 //   O^T += V^T P^T on v_mfma_f32_16x16x32_f16 with P rounded to fp16 (11-bit
-//   significand, relative error 2^-12) and V converted bf16 -> fp16 when the
-//   tile is written to LDS (exact for |v| in fp16's range; larger magnitudes
-//   saturate at 65504, a precondition of this path).
+//   significand, relative error 2^-12) and V converted bf16 -> fp16, rounding
+//   to nearest, when the tile is written to LDS: exact for |v| in
+//   [2^-14, 65504]; smaller magnitudes keep an absolute error of at most 2^-25
+//   (unbiased), larger ones overflow.  Preconditions of this path: |V| < 65504,
+//   and V not so small that 2^-25 matters (an N(0, s^2) V meets the parity bar
+//   down to s of about 1e-5).
 // The softmax denominator is the same product with V replaced by ones, so it
 // sums exactly the rounded P that weighs V and costs no VALU additions.
 #pragma once

@@ -193,11 +193,8 @@ hipError_t dispatch(const CacheWriteArgs& a, int D, int block_size, hipStream_t 
     const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
     return with_block_size(block_size, [&](auto bs) {
       constexpr int BS = decltype(bs)::value;
-      if (D == 64)
-        hipLaunchKernelGGL((cache_write_kernel<64, BS, T>), dim3(blocks), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((cache_write_kernel<128, BS, T>), dim3(blocks), dim3(kThreads), 0, s, a);
-      return hipGetLastError();
+      if (D == 64) return launch_kernel(cache_write_kernel<64, BS, T>, dim3(blocks), dim3(kThreads), 0, s, a);
+      return launch_kernel(cache_write_kernel<128, BS, T>, dim3(blocks), dim3(kThreads), 0, s, a);
     });
   }
   // groups: each sequence's new positions touch at most q_len / 16 + 2 of them
@@ -206,11 +203,8 @@ hipError_t dispatch(const CacheWriteArgs& a, int D, int block_size, hipStream_t 
   return with_block_size(block_size, [&](auto bs) {
     constexpr int BS = decltype(bs)::value;
     const dim3 grid((unsigned)groups, a.num_kv_heads);
-    if (D == 64)
-      hipLaunchKernelGGL((cache_write_group_kernel<64, BS, T>), grid, dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL((cache_write_group_kernel<128, BS, T>), grid, dim3(128), 0, s, a);
-    return hipGetLastError();
+    if (D == 64) return launch_kernel(cache_write_group_kernel<64, BS, T>, grid, dim3(64), 0, s, a);
+    return launch_kernel(cache_write_group_kernel<128, BS, T>, grid, dim3(128), 0, s, a);
   });
 }
 

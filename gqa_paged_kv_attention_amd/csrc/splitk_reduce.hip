@@ -62,11 +62,8 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(ReduceArgs a) {
 template <class OutT>
 hipError_t dispatch(const ReduceArgs& a, int D, int num_seqs, hipStream_t s) {
   dim3 grid(a.num_heads, num_seqs);
-  if (D == 64)
-    hipLaunchKernelGGL((splitk_reduce_kernel<64, OutT>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<128, OutT>), grid, dim3(128), 0, s, a);
-  return hipGetLastError();
+  if (D == 64) return launch_kernel(splitk_reduce_kernel<64, OutT>, grid, dim3(64), 0, s, a);
+  return launch_kernel(splitk_reduce_kernel<128, OutT>, grid, dim3(128), 0, s, a);
 }
 
 }  // namespace

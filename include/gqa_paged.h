@@ -226,8 +226,10 @@ int32_t splitk_lse_reduce(void* out, const float* partial_out, const float* part
  * split into partitions of partition_size tokens (merged by log-sum-exp in
  * partition order); partition_size == 0 lets the library pick (partitions of
  * 4096 tokens, i.e. no split unless max_seq_len > 4096).  Prefill rows compute
- * P.V on fp16 matrix cores (P rounded to fp16, V converted from bf16):
- * precondition |V| < 65504, else results saturate.
+ * P.V on fp16 matrix cores (P rounded to fp16, V converted from bf16 to
+ * fp16 rounding to nearest): preconditions |V| < 65504 (larger values
+ * overflow) and V not so small that fp16's subnormal spacing 2^-24 matters
+ * (for V ~ N(0, s^2) the parity bar holds down to s of about 1e-5).
  * fp32: a prefill kernel, then the decode of paged_gqa_decode (same meaning of
  * partition_size).  Either dtype: a batch whose max_query_len is 1 (decodes
  * only) runs the decode of paged_gqa_decode alone.  bf16 batches with 2^20 or more work units (num_tokens * G /
@@ -294,8 +296,8 @@ int32_t paged_cross_attention(void* out, const void* query, const void* key_cach
  * keys.  Each member's remaining keys run the decode in partitions of
  * partition_size tokens (0: the library picks, at least 256).  The partials
  * of both are merged by log-sum-exp.  The prefix tiles compute P.V on fp16
- * matrix cores as chunked_prefill_paged_decode does (precondition
- * |V| < 65504).  fp32: runs paged_gqa_decode (no sharing), with the same
+ * matrix cores as chunked_prefill_paged_decode does (same preconditions on
+ * the magnitude of V).  fp32: runs paged_gqa_decode (no sharing), with the same
  * meaning of partition_size.
  *
  * Workspace (device, >= paged_gqa_decode_shared_prefix_workspace_size bytes
