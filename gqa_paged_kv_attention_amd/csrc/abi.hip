@@ -2,6 +2,7 @@
 // sizing and kernel dispatch.  No allocation, no synchronisation, no state.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "gqa_paged.h"
 #include "gqa_internal.h"
@@ -441,6 +442,31 @@ bool shared_prefix_plan(const gqa_dims& d, int32_t num_groups, int32_t max_group
   return true;
 }
 
+// Scratch of paged_gqa_decode_noalloc: one array per device, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept here.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+
+// Device address of this device's scratch array, or nullptr if the runtime
+// cannot give one.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -452,6 +478,7 @@ const char* gqa_status_string(int32_t status) {
     case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
     case GQA_ERR_WORKSPACE: return "workspace missing or too small";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
+    case GQA_ERR_SCRATCH: return "call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -501,6 +528,26 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
     return GQA_ERR_INVALID_ARG;
   return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
                     max_seq_len, dims, scale, partition_size, workspace, workspace_bytes,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t paged_gqa_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens, int32_t max_seq_len,
+                                 gqa_dims dims, float scale, int32_t partition_size, void* stream) {
+  int st = check_dims(dims);
+  if (st != GQA_OK) return st;
+  if (dims.num_heads / dims.num_kv_heads > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (dims.num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens))
+    return GQA_ERR_INVALID_ARG;
+  int psize = 0, nparts = 0;
+  if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return GQA_ERR_INVALID_ARG;
+  if (decode_workspace(dims, max_seq_len, partition_size) > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ERR_SCRATCH;
+  if (dims.num_seqs == 0) return GQA_OK;
+  void* ws = device_scratch();
+  if (ws == nullptr) return GQA_ERR_LAUNCH;
+  return run_decode(out, query, key_cache, value_cache, block_tables, seq_lens, nullptr, dims.num_seqs,
+                    max_seq_len, dims, scale, partition_size, ws, GQA_NOALLOC_SCRATCH_BYTES,
                     reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -21,7 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gqa_paged.h")
 
 GQA_F32, GQA_BF16 = 0, 1
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
-          4: "GQA_ERR_LAUNCH"}
+          4: "GQA_ERR_LAUNCH", 5: "GQA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20          # GQA_NOALLOC_SCRATCH_BYTES
 
 
 class GqaError(RuntimeError):
@@ -58,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_decode_workspace_size.restype = sz
     lib.paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
     lib.paged_gqa_decode.restype = i32
+    lib.paged_gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp]
+    lib.paged_gqa_decode_noalloc.restype = i32
     lib.paged_gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
     lib.paged_gqa_decode_append.restype = i32
     lib.splitk_lse_reduce.argtypes = [vp, vp, vp, vp, vp, Dims, i32, i32, i32, vp]
@@ -242,6 +245,31 @@ def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_
                                                    _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
                                                    float(scale), int(partition_size), _ptr(ws), wsb,
                                                    _stream(stream)))
+    return out
+
+
+def paged_gqa_decode_noalloc(query, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+                             partition_size: int = 0, out=None, out_dtype=None, stream=None):
+    """Decode attention as paged_gqa_decode, with the library's static per-device
+    scratch in place of a workspace (the C call allocates nothing; pass ``out``
+    to allocate nothing here either)."""
+    _, hkv, _, d = _check_caches(key_cache, value_cache)
+    _check_query(query, hkv, d)
+    B, Hq, d = query.shape
+    _check_rows("out", out, B, Hq, d)
+    _check_tables(block_tables, B, seq_lens)
+    lib = load_library()
+    _check_device(query, key_cache, value_cache, block_tables, seq_lens, out)
+    _check_int32(block_tables, seq_lens)
+    out_dtype = out.dtype if out is not None else (out_dtype or torch.float32)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=query.device)
+    dims = make_dims(num_seqs=B, num_heads=Hq, key_cache=key_cache, block_tables=block_tables, q_dtype=query.dtype,
+                     out_dtype=out_dtype)
+    _call("paged_gqa_decode_noalloc",
+          lib.paged_gqa_decode_noalloc(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                       _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims, float(scale),
+                                       int(partition_size), _stream(stream)))
     return out
 
 

@@ -72,7 +72,8 @@ typedef enum {
   GQA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, num_heads % num_kv_heads != 0, ... */
   GQA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, group size or dtype combination not built */
   GQA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than *_workspace_size() */
-  GQA_ERR_LAUNCH = 4         /* the HIP runtime reported an error at launch (or no device) */
+  GQA_ERR_LAUNCH = 4,        /* the HIP runtime reported an error at launch (or no device) */
+  GQA_ERR_SCRATCH = 5        /* paged_gqa_decode_noalloc: the call needs more than GQA_NOALLOC_SCRATCH_BYTES */
 } gqa_status;
 
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
@@ -157,6 +158,30 @@ int32_t paged_gqa_decode(void* out, const void* query, const void* key_cache, co
                          const int32_t* block_tables, const int32_t* seq_lens, int32_t max_seq_len,
                          gqa_dims dims, float scale, int32_t partition_size, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * paged_gqa_decode_noalloc: paged_gqa_decode without a workspace argument, for
+ * callers that cannot allocate device memory around the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * split partials and metadata live in a static device array of
+ * GQA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the call allocates nothing and calls no allocating
+ * routine.  Same arguments, kernels and results as paged_gqa_decode with a
+ * workspace of that size.
+ *
+ * Returns GQA_ERR_SCRATCH, before any launch, when
+ * paged_gqa_decode_workspace_size(dims, max_seq_len, partition_size) exceeds
+ * GQA_NOALLOC_SCRATCH_BYTES.  The array's device address is looked up once per
+ * device, at the first call on that device (GQA_ERR_LAUNCH if that fails).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or host threads) race on it and must be serialised by
+ * the caller.  No kernel needs the array cleared: each call writes what it
+ * reads.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t paged_gqa_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens, int32_t max_seq_len,
+                                 gqa_dims dims, float scale, int32_t partition_size, void* stream);
 
 /*
  * paged_gqa_decode_append: one decode step with the cache write fused in.

@@ -201,3 +201,19 @@ def test_shared_prefix_validation(lib):
     f32 = dims(q_dtype=ops.GQA_F32, kv_dtype=ops.GQA_F32)
     assert lib.paged_gqa_decode_shared_prefix_workspace_size(f32, 2, 4, 4096, 512) == \
         lib.paged_gqa_decode_workspace_size(f32, 4096, 512)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """paged_gqa_decode_noalloc checks the call's scratch need against its fixed
+    static buffer on the host, before any device call: 4096 sequences x 64
+    heads in 8 partitions need 1 GiB of partials."""
+    assert lib.gqa_status_string(5) == b"call needs more scratch than the library's static buffer holds"
+    big = dims(num_seqs=4096, num_heads=64, num_kv_heads=8, max_blocks_per_seq=256)
+    assert lib.paged_gqa_decode_workspace_size(big, 4096, 512) > ops.NOALLOC_SCRATCH_BYTES
+    assert lib.paged_gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, big, 0.1, 512, None) == 5
+    # argument errors come first, as in paged_gqa_decode
+    assert lib.paged_gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, dims(num_kv_heads=7), 0.1, 0,
+                                        None) == INVALID
+    assert lib.paged_gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, dims(), 0.1, 48, None) == INVALID
+    # no sequences: nothing to do, nothing looked up
+    assert lib.paged_gqa_decode_noalloc(None, None, None, None, None, None, 0, dims(num_seqs=0), 0.1, 0, None) == OK
