@@ -66,6 +66,10 @@ def parse():
                     help="skip the unfused step and the plain decode call (so that a profiler sees the step only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 512 MiB device copy and exit")
+    ap.add_argument("--profile-leg", choices=sorted(PROFILE_LEGS), default=None,
+                    help="run only this leg's call --profile-calls times (no timing, no JSON line): a short "
+                         "program for rocprofv3 counter passes")
+    ap.add_argument("--profile-calls", type=int, default=20)
     return ap.parse_args()
 
 
@@ -139,10 +143,10 @@ def cold_times_ms(fn, reps, stream, flush):
     return {"p10_ms": round(float(p10), 5), "p50_ms": round(float(p50), 5), "p90_ms": round(float(p90), 5)}
 
 
-def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
-    """chunked_prefill_paged_decode on the sequences `idx` of the mixed batch
-    alone (their query rows, block-table rows and lengths; the same caches and
-    pages), bf16 output: ms per call."""
+def mixed_part_call(mb, idx, mq, mkc, mvc, mt, ml, dev):
+    """A callable running chunked_prefill_paged_decode on the sequences `idx` of
+    the mixed batch alone (their query rows, block-table rows and lengths; the
+    same caches and pages), bf16 output."""
     import torch
     from gqa_paged_kv_attention_amd import ops
     idx = np.asarray(idx, dtype=np.int64)
@@ -160,10 +164,76 @@ def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
     dims = ops.make_dims(num_seqs=len(idx), num_heads=mb.num_heads, key_cache=mkc, block_tables=tb, q_dtype=q.dtype,
                          out_dtype=out.dtype)
     ws = torch.zeros(max(ops.mixed_workspace_size(dims, T, max_sl, 0), 1), dtype=torch.uint8, device=dev)
-    f = lambda: ops.chunked_prefill_paged_decode(q, mkc, mvc, tb, sl, s_qsl, int(ql.max()), max_sl, mb.scale,
-                                                 partition_size=0, out=out, workspace=ws)
+    return lambda: ops.chunked_prefill_paged_decode(q, mkc, mvc, tb, sl, s_qsl, int(ql.max()), max_sl, mb.scale,
+                                                    partition_size=0, out=out, workspace=ws)
+
+
+def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
+    """ms per call of mixed_part_call's callable."""
+    f = mixed_part_call(mb, idx, mq, mkc, mvc, mt, ml, dev)
     warm_up(f, stream)
     return event_time_ms(f, reps, stream)
+
+
+# Legs that --profile-leg can run alone (workload, call):
+#   decode_step    the headline step (paged_gqa_decode_append, llama31_8b_decode)
+#   mixed          chunked_prefill_paged_decode on the whole mixed batch, bf16 output
+#   mixed_prefill  the mixed batch's 51 prefill chunks alone, same call
+#   mixed_decode   the mixed batch's 205 decodes alone, same call
+#   longctx512     16 x 32k tokens, paged_gqa_decode with 512-token partitions
+#   longctx        the same with the library's split
+PROFILE_LEGS = ("decode_step", "mixed", "mixed_prefill", "mixed_decode", "longctx512", "longctx")
+
+
+def profile_leg(name, calls, dev, stream, seed):
+    """Build one leg's inputs, run its call once, then `calls` more times; print one line."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    from gqa_paged_kv_attention_amd import workloads as wl
+    up = lambda a: ops.to_device(a, dev)
+    if name == "decode_step":
+        bt = wl.llama31_8b_decode(seed=seed)
+        q, kc, vc, nk, nv = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.new_key), up(bt.new_value)
+        tb, sl = up(bt.block_tables), up(bt.seq_lens)
+        out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        f = lambda: ops.paged_gqa_decode_append(q, nk, nv, kc, vc, tb, sl, bt.max_seq_len, bt.scale, out=out)
+    elif name.startswith("mixed"):
+        mb = wl.mixed_chunked(seed=4)
+        mq, mkc, mvc = up(mb.query), up(mb.key_cache), up(mb.value_cache)
+        mt, ml, mqsl = up(mb.block_tables), up(mb.seq_lens), up(mb.query_start_loc)
+        ops.reshape_and_cache(up(mb.new_key), up(mb.new_value), mkc, mvc, mt, ml, mqsl)
+        ql = mb.query_lens.astype(np.int64)
+        idx = {"mixed": np.arange(mb.num_seqs), "mixed_prefill": np.where(ql > 1)[0],
+               "mixed_decode": np.where(ql == 1)[0]}[name]
+        f = mixed_part_call(mb, idx, mq, mkc, mvc, mt, ml, dev)
+    else:
+        bt = wl.longctx_splitk(seed=5)
+        q, kc, vc, tb, sl = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.block_tables), up(bt.seq_lens)
+        out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        part = 512 if name == "longctx512" else 0
+        f = lambda: ops.paged_gqa_decode(q, kc, vc, tb, sl, bt.max_seq_len, bt.scale, partition_size=part, out=out)
+    f()
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        f()
+    torch.cuda.synchronize()
+    print(f"profile leg {name}: {calls} calls after one warm-up call", flush=True)
+
+
+def measured_mfma_peak(dev, stream):
+    """bf16 matrix-core rate this device sustains: the library's probe (8 waves
+    per compute unit, 8 independent chains of v_mfma_f32_16x16x32_bf16 each),
+    timed with HIP events after a warm-up.  TFLOP/s."""
+    import torch
+    from gqa_paged_kv_attention_amd import ops
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    groups, iters = 2 * cus, 4000
+    out = torch.empty(4 * groups, dtype=torch.float32, device=dev)
+    flops = ops.probe_mfma_bf16(out, groups, iters, stream)
+    f = lambda: ops.probe_mfma_bf16(out, groups, iters, stream)
+    warm_up(f, stream)
+    ms = min(event_time_ms(f, 10, stream) for _ in range(3))
+    return round(flops / (ms * 1e-3) / 1e12, 1)
 
 
 def stream_copy_gbs(buf, stream, reps=20):
@@ -289,7 +359,7 @@ def cross_attention_leg(dev, stream, reps):
     return res
 
 
-def long_context_leg(dev, stream, reps):
+def long_context_leg(dev, stream, reps, flush=None):
     """Long-context split-K decode: 16 sequences of 32768 tokens, Hq=64, Hkv=8,
     d=128, bf16 (2.15 GB of K+V), with 512-token partitions merged by
     log-sum-exp (splitk_lse_reduce inside the call) and with the split the
@@ -314,8 +384,10 @@ def long_context_leg(dev, stream, reps):
         warm_up(f, stream)
         ms = event_time_ms(f, reps, stream)
         gbs = bt.kv_bytes() / (ms * 1e-3) / 1e9
-        res["partition_512" if part else "library_split"] = {"us": round(ms * 1e3, 2), "kv_gbs": round(gbs, 1),
-                                                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        leg = {"us": round(ms * 1e3, 2), "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if flush is not None:
+            leg["cold"] = cold_times_ms(f, 10, stream, flush)
+        res["partition_512" if part else "library_split"] = leg
         del ws
     del q, kc, vc, out
     return res
@@ -442,6 +514,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.profile_leg:
+        profile_leg(args.profile_leg, args.profile_calls, dev, stream, args.seed)
+        return
 
     bt = wl.llama31_8b_decode(seed=args.seed)
     up = lambda a: ops.to_device(a, dev)
@@ -545,7 +620,10 @@ def main():
                                                  workspace=mws)
             warm_up(mixed, stream)
             times[name] = event_time_ms(mixed, 50, stream)
+            if name == "bf16":
+                mixed_cold = cold_times_ms(mixed, 20, stream, flush)
         mixed_ms = times["bf16"]
+        mfma_peak = measured_mfma_peak(dev, stream)
         # diagnostics: each part of the batch alone through the same entry point
         pf_idx, dec_idx = np.where(ql > 1)[0], np.where(ql == 1)[0]
         pf_flops = 4 * mb.head_dim * mb.num_heads * int(np.sum(ql[pf_idx] * prior[pf_idx] +
@@ -558,6 +636,9 @@ def main():
                                  "tokens_per_s": round(mb.num_tokens / (mixed_ms * 1e-3), 1),
                                  "algorithmic_gflop": round(flops / 1e9, 3),
                                  "mfma_util": round(flops / (mixed_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+                                 "measured_mfma_peak_tflops": mfma_peak,
+                                 "mfma_util_vs_measured_peak": round(flops / (mixed_ms * 1e-3) / (mfma_peak * 1e12), 4),
+                                 "cold": dict(mixed_cold, note="each call alone after a 1 GiB read (caches flushed)"),
                                  "kv_gb": round(mb.kv_bytes() / 1e9, 4),
                                  # K/V once, queries once, outputs once: the batch's least HBM traffic
                                  "min_hbm_gb": round((mb.kv_bytes() + rows * 2 + rows * 2) / 1e9, 4),
@@ -586,7 +667,7 @@ def main():
         record["shared_prefix"] = shared_prefix_leg(dev, stream, 30)
 
     if not args.no_long_context:
-        record["long_context"] = long_context_leg(dev, stream, 20)
+        record["long_context"] = long_context_leg(dev, stream, 20, flush)
 
     if not args.no_cache_write:
         record["cache_write"] = cache_write_leg(dev, stream, 50, args.seed)

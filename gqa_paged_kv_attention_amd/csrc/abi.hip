@@ -483,7 +483,13 @@ const char* gqa_status_string(int32_t status) {
   }
 }
 
-int32_t gqa_version(void) { return 100; }
+int32_t gqa_version(void) { return 101; }
+
+int32_t gqa_probe_mfma_bf16(float* out, int32_t groups, int32_t iters, long long* flops, void* stream) {
+  if (!out || !flops || groups <= 0 || iters <= 0) return GQA_ERR_INVALID_ARG;
+  *flops = gqa::mfma_probe_flops(groups, iters);
+  return status_from(gqa::launch_mfma_probe(out, groups, iters, reinterpret_cast<hipStream_t>(stream)));
+}
 
 int32_t reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                           const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,

@@ -6,13 +6,14 @@
 
 namespace gqa {
 
-// Launch kernel k (whose one parameter is a struct passed by value) and return
-// the status of this launch alone.  hipLaunchKernel reports its own result, so
-// an error left pending by the caller's earlier HIP calls is neither read as
-// this launch's nor cleared.
-template <class Args>
-inline hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, size_t lds, hipStream_t s, const Args& a) {
-  void* args[] = {const_cast<Args*>(&a)};
+// Launch kernel k with its arguments (passed by value) and return the status
+// of this launch alone.  hipLaunchKernel reports its own result, so an error
+// left pending by the caller's earlier HIP calls is neither read as this
+// launch's nor cleared.
+template <class... P, class... A>
+inline hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, const A&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one value per kernel parameter");
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))...};
   return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, lds, s);
 }
 
@@ -212,5 +213,9 @@ hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool o
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, int block_size, bool kv_f32,
                               hipStream_t stream);
+// Measurement probe: `groups` work-groups of 4 waves issue bf16 matrix-core
+// products for `iters` rounds; mfma_probe_flops gives the flops of one launch.
+hipError_t launch_mfma_probe(float* out, int groups, int iters, hipStream_t stream);
+long long mfma_probe_flops(int groups, int iters);
 
 }  // namespace gqa

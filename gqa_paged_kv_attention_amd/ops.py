@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_decode_workspace_size.restype = sz
     lib.paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
     lib.paged_gqa_decode.restype = i32
+    lib.gqa_probe_mfma_bf16.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_longlong), vp]
+    lib.gqa_probe_mfma_bf16.restype = i32
     lib.paged_gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp]
     lib.paged_gqa_decode_noalloc.restype = i32
     lib.paged_gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, Dims, f32, i32, vp, sz, vp]
@@ -436,6 +438,19 @@ def paged_gqa_decode_shared_prefix(query, key_cache, value_cache, block_tables, 
                                              dims, float(scale), int(partition_size), _ptr(ws), wsb,
                                              _stream(stream)))
     return out
+
+
+def probe_mfma_bf16(out: torch.Tensor, groups: int, iters: int, stream=None) -> int:
+    """Enqueue the library's bf16 matrix-core rate probe (a measurement aid, not
+    part of the attention path); returns the launch's flops."""
+    lib = load_library()
+    _check_device(out)
+    if out.dtype != torch.float32 or out.numel() < 4 * groups:
+        raise ValueError("out must be float32 with at least 4 * groups elements")
+    flops = ctypes.c_longlong(0)
+    _call("gqa_probe_mfma_bf16", lib.gqa_probe_mfma_bf16(_ptr(out), int(groups), int(iters), ctypes.byref(flops),
+                                                         _stream(stream)))
+    return int(flops.value)
 
 
 def to_device(arr, device="cuda") -> torch.Tensor:

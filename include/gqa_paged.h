@@ -98,6 +98,17 @@ const char* gqa_status_string(int32_t status);
 int32_t gqa_version(void);
 
 /*
+ * gqa_probe_mfma_bf16: a measurement probe, not part of the attention path.
+ * Enqueues `groups` work-groups of 4 waves, each wave issuing `iters` rounds
+ * of 8 independent v_mfma_f32_16x16x32_bf16 products, and writes one float per
+ * wave to out[groups * 4] (device).  *flops (host) receives the launch's
+ * multiply-add flops (2 per multiply-add), so that flops / elapsed time is the
+ * bf16 matrix rate this device sustains.  GQA_ERR_INVALID_ARG for a null
+ * pointer or non-positive sizes.
+ */
+int32_t gqa_probe_mfma_bf16(float* out, int32_t groups, int32_t iters, long long* flops, void* stream);
+
+/*
  * reshape_and_cache: copy this step's keys and values into the paged caches.
  * New token j of sequence b (row query_start_loc[b] + j of key/value) goes to
  * position pos = seq_lens[b] - q_len + j, i.e. page block_tables[b][pos / bs],

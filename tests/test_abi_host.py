@@ -217,3 +217,10 @@ def test_noalloc_rejects_calls_beyond_its_scratch(lib):
     assert lib.paged_gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, dims(), 0.1, 48, None) == INVALID
     # no sequences: nothing to do, nothing looked up
     assert lib.paged_gqa_decode_noalloc(None, None, None, None, None, None, 0, dims(num_seqs=0), 0.1, 0, None) == OK
+
+
+def test_mfma_probe_rejects_bad_arguments(lib):
+    flops = ctypes.c_longlong(0)
+    assert lib.gqa_probe_mfma_bf16(None, 4, 10, ctypes.byref(flops), None) == INVALID
+    assert lib.gqa_probe_mfma_bf16(FAKE, 0, 10, ctypes.byref(flops), None) == INVALID
+    assert lib.gqa_probe_mfma_bf16(FAKE, 4, 0, ctypes.byref(flops), None) == INVALID
