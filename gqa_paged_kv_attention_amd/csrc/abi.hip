@@ -74,6 +74,22 @@ bool use_stream(const gqa_dims& d, int32_t partition_size) {
   return (long long)d.num_seqs * d.num_kv_heads < 2 * resident_groups;
 }
 
+// Fixed partitions (partition_size > 0) with G <= 16 run the partitioned
+// balanced decode: persistent waves walk whole partitions back to back, their
+// load pipeline running across partition boundaries, instead of one
+// work-group per partition.  Same partials, same workspace, same reduce.
+// The kernel's LDS (a 32-row partial buffer per wave plus the per-sequence
+// tables) leaves room for two work-groups per compute unit up to
+// kMaxPartitionedSeqs sequences; buffered partial rows are int indices.
+constexpr int kMaxPartitionedSeqs = 1536;
+bool use_stream_partitioned(const gqa_dims& d, int32_t partition_size, int nparts) {
+  if (partition_size <= 0 || nparts <= 1 || d.num_seqs == 0 || d.num_seqs > kMaxPartitionedSeqs) return false;
+  if (d.num_heads / d.num_kv_heads > 16) return false;
+  if ((long long)d.num_seqs * d.num_heads * nparts >= (1LL << 31) - 1) return false;
+  const long long tiles_per_seq = ((long long)d.max_blocks_per_seq * d.block_size + kTileTokens - 1) / kTileTokens;
+  return (long long)d.num_seqs * d.num_kv_heads * tiles_per_seq < (1LL << 31) - 1;
+}
+
 // Balanced-decode workspace: [tile prefix, B + 1 ints][unit metadata, B * Hkv int4]
 // [segment outputs][segment lse][whole-unit outputs, B * Hq * D][whole-unit lse, B * Hq]
 // (the last two serve the fused append).
@@ -231,7 +247,16 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   a.partition_size = psize;
   a.max_partitions = nparts;
   a.scale_log2 = scale_log2;
-  hipError_t e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, stream);
+  hipError_t e;
+  if (use_stream_partitioned(dims, partition_size, nparts)) {
+    gqa::StreamPartArgs sp;
+    sp.d = a;
+    sp.num_seqs = dims.num_seqs;
+    sp.num_workers = gqa::partition_workers(dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs);
+    e = gqa::launch_stream_partition(sp, dims.head_dim, dims.block_size, kv_f32, out_f32, stream);
+  } else {
+    e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, stream);
+  }
   if (e != hipSuccess || nparts <= 1) return status_from(e);
   gqa::ReduceArgs r;
   r.out = out;

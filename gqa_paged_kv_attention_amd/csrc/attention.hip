@@ -327,6 +327,204 @@ __global__ __launch_bounds__(D) void stream_reduce_kernel(StreamArgs a) {
   if (fold && g == 0) append_store<D, InT>(a, b, kv, d);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced decode in fixed partitions (partition_size > 0, G <= 16).  Each
+// decode unit (sequence, kv head) of nt 32-token tiles is split into
+// np = ceil(nt / PT) partitions of nearly equal length (PT = partition_size /
+// 32; the split decode_partition_at uses).  Units are laid out as in the
+// balanced decode; worker (wave) w owns the partitions that start in
+// [snap(T w / W), snap(T (w + 1) / W)), snap moving a tile position forward to
+// the next partition start, so every partition belongs to exactly one worker
+// and the tiles are balanced up to one partition per worker.  A wave walks its
+// partitions' tiles as one stream: the paired load pipeline runs across
+// partition boundaries.  When a partition is complete the wave puts its
+// normalised output and log-sum-exp into an LDS buffer (kPartRows rows per
+// wave) and resets its softmax state; the buffer goes to the split-K partials
+// in global memory when it is full and when the wave has walked its range.
+// Partials stored as each partition ended, inside the HBM read stream, cost 40
+// us on 16 x 32k tokens (409 against 369 us without them); written in bursts
+// at the end, with the non-temporal hint, they overlap the other waves' last
+// reads (409 -> 389 us, and 384 us with the hint).  A sequence of one
+// partition writes `out` directly.  splitk_reduce_kernel merges the partials.
+// ---------------------------------------------------------------------------
+
+constexpr int kPartRows = 32;           // rows of partials a wave buffers in LDS
+
+// First tile of partition p of a unit of nt tiles in np partitions.
+__device__ __forceinline__ int part_first_tile(int p, int nt, int np) {
+  const int per = nt / np, extra = nt % np;
+  return p * per + min(p, extra);
+}
+
+// Index of the first partition that starts at or after tile offset off (np
+// when off is past the last start); the first `extra` partitions hold per + 1
+// tiles, the others per (per >= 1 since np <= nt).
+__device__ __forceinline__ int part_at_or_after(int off, int nt, int np) {
+  const int per = nt / np, extra = nt % np;
+  const int big = extra * (per + 1);
+  if (off <= big) return (off + per) / (per + 1);
+  return extra + (off - big + per - 1) / per;
+}
+
+// Largest b in [0, B) with s_pref[b] <= t (s_pref non-decreasing, s_pref[0] = 0 <= t).
+__device__ __forceinline__ int seq_of_item(const int* s_pref, int B, long long t) {
+  int bl = 0, bh = B;
+  while (bh - bl > 1) {
+    const int mid = (bl + bh) >> 1;
+    if (s_pref[mid] <= t) bl = mid; else bh = mid;
+  }
+  return bl;
+}
+
+template <class Tile, int D, class OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, 1>())))
+void stream_partition_kernel(StreamPartArgs sp) {
+  // partial buffer: per wave kPartRows rows of D floats, their lse, and the
+  // target row (index into the [B * Hq, max_partitions] partial rows) of
+  // each buffered partition
+  __shared__ __attribute__((aligned(16))) float s_part[kWaves][kPartRows][D];
+  __shared__ float s_plse[kWaves][kPartRows];
+  __shared__ int s_ptgt[kWaves][kPartRows];
+  extern __shared__ int s_pref[];          // [B + 1] exclusive prefix of tiles * Hkv, then s_len [B]
+  __shared__ int s_scan[kWaves];
+  const DecodeArgs& a = sp.d;
+  const int B = sp.num_seqs, G = a.group, Hkv = a.num_kv_heads;
+  int* s_len = s_pref + B + 1;
+  const int lane = lane_id();
+  const int n = lane & 15, q = lane >> 4;
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  const int PT = a.partition_size / kTile;
+
+  // ---- prefix of per-sequence tiles x Hkv, in chunks of kThreads sequences ----
+  int running = 0;
+  for (int c0 = 0; c0 < B; c0 += kThreads) {
+    const int b = c0 + threadIdx.x;
+    int v = 0;
+    if (b < B) {
+      int row = b;
+      bool dec = true;
+      if (a.query_start_loc) {
+        const int q0 = a.query_start_loc[b], q1 = a.query_start_loc[b + 1];
+        row = q0;
+        dec = q1 - q0 == 1 && q1 <= a.num_tokens && q0 >= 0;
+      }
+      const int L = dec ? min(clamp_len(a.seq_lens[b], a.max_blocks_per_seq, Tile::kBS),
+                              a.max_partitions * a.partition_size)
+                        : 0;
+      v = (L + kTile - 1) / kTile * Hkv;
+      s_len[b] = L;
+      if (dec && L == 0 && (b % gridDim.x) == (int)blockIdx.x)
+        for (int i = 0; i < a.num_heads * D; ++i) store1(out + (size_t)row * a.num_heads * D + i, 0.f);
+    }
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    const int wv = wave_id();
+    if (lane == kWave - 1) s_scan[wv] = x;
+    __syncthreads();
+    int base = running;
+    for (int i = 0; i < wv; ++i) base += s_scan[i];
+    if (b < B) s_pref[b + 1] = base + x;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) running += s_scan[i];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  __syncthreads();
+
+  const long long T = s_pref[B];
+  const int W = sp.num_workers;
+  // next partition start at or after item position t (T at the end)
+  auto snap = [&](long long t) -> long long {
+    if (t >= T) return T;
+    const int b = seq_of_item(s_pref, B, t);
+    const int nt = (s_pref[b + 1] - s_pref[b]) / Hkv;
+    const int in_seq = (int)(t - s_pref[b]);
+    const int kv = in_seq / nt, off = in_seq % nt;
+    const int np = (nt + PT - 1) / PT;
+    return s_pref[b] + (long long)kv * nt + part_first_tile(part_at_or_after(off, nt, np), nt, np);
+  };
+  const int w = blockIdx.x * kWaves + wave_id();
+  const long long start = snap(T * w / W), end = snap(T * (w + 1) / W);
+  const int wv = wave_id();
+  const int per_buf = kPartRows / G;       // partitions the wave's buffer holds (G <= 16 <= kPartRows)
+  int nbuf = 0;
+  // write the wave's buffered partitions to the partials: two rows of D
+  // floats per 16-byte store instruction, then the lse values
+  auto drain = [&]() {
+    for (int i = lane; i < nbuf * G * (D / 4); i += kWave) {
+      const int r = i / (D / 4), c = 4 * (i % (D / 4));
+      const int j = r / G, g = r % G;
+      const size_t row = (size_t)s_ptgt[wv][j] + (size_t)g * a.max_partitions;
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(&s_part[wv][r][c]),
+                                  reinterpret_cast<f32x4_t*>(a.partial_out + row * D + c));
+    }
+    for (int r = lane; r < nbuf * G; r += kWave)
+      a.partial_lse[(size_t)s_ptgt[wv][r / G] + (size_t)(r % G) * a.max_partitions] = s_plse[wv][r];
+    nbuf = 0;
+  };
+  long long t = start;
+  while (t < end) {
+    const int b = uniform(seq_of_item(s_pref, B, t));
+    const int nt = (s_pref[b + 1] - s_pref[b]) / Hkv;
+    const int in_seq = (int)(t - s_pref[b]);
+    const int kv = in_seq / nt, tile_begin = in_seq % nt;
+    const long long unit0 = s_pref[b] + (long long)kv * nt;
+    const int tile_end = (int)min((long long)nt, end - unit0);
+    const int np = (nt + PT - 1) / PT;
+    const int L = s_len[b];
+    const int row = a.query_start_loc ? a.query_start_loc[b] : b;
+
+    typename Tile::Q qf[1];
+    load_group_query<Tile, D, 1>(qf, a.query, row, a.num_heads, kv, G, lane);
+    WaveState<Tile, 1> st;
+    st.reset();
+    const size_t head0 = (size_t)b * a.num_heads + kv * G;
+    int p = part_at_or_after(tile_begin, nt, np);          // tile_begin is a partition start
+    int p_end = part_first_tile(p + 1, nt, np);
+    // write partition p's partial, reset the state, move on to partition p + 1
+    auto flush = [&]() {
+      const int g = n;
+      const float lr = row_sum4(st.l[0]);
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      if (np == 1) {
+        if (g < G) {
+          OutT* dst = out + ((size_t)row * a.num_heads + kv * G + g) * D + 4 * q;
+#pragma unroll
+          for (int dt = 0; dt < Tile::DT; ++dt) store4(dst + dt * 16, st.o[0][dt] * inv);
+        }
+      } else {
+        if (nbuf == per_buf) drain();
+        if (g < G) {
+          const int r = nbuf * G + g;
+#pragma unroll
+          for (int dt = 0; dt < Tile::DT; ++dt) {
+            const f32x4_t v = st.o[0][dt] * inv;
+            *reinterpret_cast<float4*>(&s_part[wv][r][dt * 16 + 4 * q]) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+          if (q == 0) s_plse[wv][r] = lr > 0.f ? (st.m[0] + __log2f(lr)) * kLn2 : -INFINITY;
+        }
+        if (lane == 0) s_ptgt[wv][nbuf] = (int)(head0 * a.max_partitions + p);
+        ++nbuf;
+      }
+      st.reset();
+      ++p;
+      p_end = part_first_tile(p + 1, nt, np);
+    };
+    auto before = [&](int tile) {
+      if (tile == p_end) flush();                          // partition p ended with tile - 1
+    };
+    run_tiles<Tile, D, 1>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
+                          a.num_blocks, Hkv, kv, L, L - 1, tile_begin, tile_end, 1, a.scale_log2, lane, before);
+    flush();                                               // the range ends with a partition's last tile
+    t = unit0 + tile_end;
+  }
+  drain();
+}
+
 template <int NTW>
 struct PrefillShape {
   static constexpr int kRowsPerWave = NTW * 16;
@@ -490,21 +688,19 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bo
   });
 }
 
-// Workers of the balanced decode: compute units x resident work-groups per
-// compute unit x 4 waves.  The compute-unit count and the kernel's occupancy
-// are queried once per (device, kernel, 1 KiB step of its dynamic LDS) and
-// cached: workspace queries and decode calls then make no runtime query beyond
-// hipGetDevice.  The occupancy is taken at the top of the LDS step, so it never
-// exceeds what the launch's actual LDS allows.
-int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs) {
+// Resident waves of a persistent decode kernel: compute units x resident
+// work-groups per compute unit x 4 waves.  The compute-unit count and the
+// kernel's occupancy are queried once per (device, kernel, 1 KiB step of its
+// dynamic LDS) and cached: workspace queries and decode calls then make no
+// runtime query beyond hipGetDevice.  The occupancy is taken at the top of the
+// LDS step, so it never exceeds what the launch's actual LDS allows.
+int resident_workers(const void* kernel, size_t lds_bytes) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  const size_t lds_step = ((size_t)(2 * num_seqs + 1) * sizeof(int) + 1023) / 1024;
-  void (*kernel)(StreamArgs) =
-      with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [](void (*k)(StreamArgs)) { return k; });
+  const size_t lds_step = (lds_bytes + 1023) / 1024;
   static std::mutex mu;
   static std::map<std::tuple<int, const void*, size_t>, int> cache;
-  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kernel), lds_step);
+  const auto key = std::make_tuple(dev, kernel, lds_step);
   {
     std::lock_guard<std::mutex> lock(mu);
     const auto it = cache.find(key);
@@ -515,14 +711,42 @@ int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int 
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(kernel), kThreads,
-                                                     lds_step * 1024) == hipSuccess && blocks > 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kThreads, lds_step * 1024) == hipSuccess &&
+        blocks > 0)
       per_cu = blocks;
   }
   const int workers = cus * per_cu * kWaves;
   std::lock_guard<std::mutex> lock(mu);
   cache[key] = workers;
   return workers;
+}
+
+int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs) {
+  void (*kernel)(StreamArgs) =
+      with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [](void (*k)(StreamArgs)) { return k; });
+  return resident_workers(reinterpret_cast<const void*>(kernel), (size_t)(2 * num_seqs + 1) * sizeof(int));
+}
+
+// The partitioned balanced decode's instantiation for (D, page size, dtype, out dtype).
+void (*partition_kernel(int head_dim, int block_size, bool kv_f32, bool out_f32))(StreamPartArgs) {
+  typedef void (*K)(StreamPartArgs);
+  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+    typedef decltype(tile) Tile;
+    constexpr int DD = decltype(dd)::value;
+    return out_f32 ? (K)stream_partition_kernel<Tile, DD, float> : (K)stream_partition_kernel<Tile, DD, uint16_t>;
+  });
+}
+
+int partition_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs) {
+  return resident_workers(reinterpret_cast<const void*>(partition_kernel(head_dim, block_size, kv_f32, out_f32)),
+                          (size_t)(2 * num_seqs + 1) * sizeof(int));
+}
+
+hipError_t launch_stream_partition(const StreamPartArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                                   hipStream_t stream) {
+  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+  return launch_kernel(partition_kernel(head_dim, block_size, kv_f32, out_f32), dim3(a.num_workers / kWaves),
+                       dim3(kThreads), lds, stream, a);
 }
 
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,

@@ -159,11 +159,20 @@ __device__ __forceinline__ void compute_tile(WaveState<Tile, NT>& st, const type
 // Prefetches past the last tile repeat it (its re-read hits in cache), which
 // keeps the load count per round fixed and lets the compiler wait on just the
 // tile about to be computed.  Register and page-set indices are literals at
-// every call of the callbacks, so the selects below fold away.
-template <class Tile, int D, int NT>
+// every call of the callbacks, so the selects below fold away.  `before(tile)`
+// runs just before each tile is computed, in tile order, after that tile's
+// loads were issued: the partitioned decode writes the previous partition's
+// partial there, so that the next wait on a load does not also wait for those
+// stores (loads and stores complete in order on one counter).
+struct NoBefore {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <class Tile, int D, int NT, class Before = NoBefore>
 __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typename Tile::Q qf[NT], const void* kc,
                                           const void* vc, const int32_t* bt, int num_blocks, int num_kv_heads, int kv,
-                                          int L, int lim, int it0, int it1, int step, float scale_log2, int lane) {
+                                          int L, int lim, int it0, int it1, int step, float scale_log2, int lane,
+                                          Before before = Before()) {
   if (it0 >= it1) return;
   // at least one page: a fused append walks the tile of its only key with L = 0
   const int npages = max(1, (L + Tile::kBS - 1) / Tile::kBS);
@@ -177,6 +186,7 @@ __device__ __forceinline__ void run_tiles(WaveState<Tile, NT>& st, const typenam
     load_tile<Tile, D>(r == 0 ? kA : kB, r == 0 ? vA : vB, p == 0 ? pa : pb, kc, vc, num_kv_heads, kv, lane);
   };
   auto compute = [&](int r, int tile) __attribute__((always_inline)) {
+    before(tile);
     compute_tile<Tile, NT>(st, qf, r == 0 ? kA : kB, r == 0 ? vA : vB, tile * kTile, L, lim, scale_log2, lane);
   };
   tile_schedule(it0, it1, step, Tile::kPipelined ? kPaired : kSingle, fetch, load, compute);

@@ -114,6 +114,21 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load with the non-temporal hint, for K/V pages that a call reads
+// once: the lines stream through instead of displacing others in L2 and the
+// Infinity Cache.  On the Llama-3.1-8B decode batch (633 MB of K/V) the
+// decode call went from 125.8 to 111.9 us with it; on 16 x 32k tokens from
+// 373 to 340 us.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ float4 ld16f_stream(const float* p) {
+  const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Max / sum across the four lane groups that share a row (lanes n, n+16,
@@ -168,6 +183,11 @@ __device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_b
 template <int D, int BS>
 struct TileBF16 {
   static constexpr int kBS = BS;
+  // Value loads stream (non-temporal) unless one 128-byte line of a channel
+  // holds both tiles of a pair (64-token pages): the second tile's half of
+  // the line must still be in L2 when it is asked for (with the hint, 64-token
+  // pages went from 129 to 152 us on the Llama-3.1-8B decode batch).
+  static constexpr bool kStreamV = BS * 2 <= 64;
   static constexpr bool kPipelined = true;  // double-buffered tile loop
   static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
   static constexpr int DT = D / 16;   // 16-channel blocks of the output
@@ -188,7 +208,7 @@ struct TileBF16 {
       const int slot = (m & 3) + 8 * ((m >> 2) & 1) + 4 * s;
       const elem_t* row = pg + slot * D + 8 * q;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) k.v[s][c] = ld16(row + 32 * c);
+      for (int c = 0; c < KC; ++c) k.v[s][c] = ld16_stream(row + 32 * c);
     }
   }
 
@@ -199,7 +219,7 @@ struct TileBF16 {
     const elem_t* pg = (q < 2) ? vA : vB;
     const elem_t* base = pg + n * BS + 8 * (q & 1);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) v.v[dt] = ld16(base + dt * 16 * BS);
+    for (int dt = 0; dt < DT; ++dt) v.v[dt] = kStreamV ? ld16_stream(base + dt * 16 * BS) : ld16(base + dt * 16 * BS);
   }
 
   // row: query row base ([D] elements) or nullptr for a padding row.
@@ -294,7 +314,7 @@ struct TileF32 {
     for (int s = 0; s < 2; ++s) {
       const elem_t* row = (s ? kB : kA) + m * D + 4 * q;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) k.v[s][c] = *reinterpret_cast<const float4*>(row + 16 * c);
+      for (int c = 0; c < KC; ++c) k.v[s][c] = ld16f_stream(row + 16 * c);
     }
   }
 
@@ -304,7 +324,8 @@ struct TileF32 {
     for (int s = 0; s < 2; ++s) {
       const elem_t* base = (s ? vB : vA) + n * BS + 4 * q;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) v.v[s][dt] = *reinterpret_cast<const float4*>(base + dt * 16 * BS);
+      for (int dt = 0; dt < DT; ++dt)
+        v.v[s][dt] = BS * 4 <= 64 ? ld16f_stream(base + dt * 16 * BS) : *reinterpret_cast<const float4*>(base + dt * 16 * BS);
     }
   }
 

@@ -71,6 +71,16 @@ struct StreamArgs {
   float scale_log2;
 };
 
+// Balanced decode in fixed partitions: persistent waves walk contiguous runs
+// of whole partitions (balanced by tiles) and write one partial per partition
+// into d.partial_out / d.partial_lse ([B, Hq, max_partitions, D] and
+// [B, Hq, max_partitions]); a sequence of one partition writes d.out.
+struct StreamPartArgs {
+  DecodeArgs d;
+  int num_seqs;
+  int num_workers;                  // 4 per work-group
+};
+
 struct PrefillArgs {
   void* out;
   const void* query;
@@ -131,6 +141,10 @@ int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int 
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
                                 hipStream_t stream);
 hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream);
+// Resident waves of the partitioned balanced decode, and its launch (a.num_workers / 4 work-groups).
+int partition_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs);
+hipError_t launch_stream_partition(const StreamPartArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
+                                   hipStream_t stream);
 // Rows per prefill work-group (depends only on the build).
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,

@@ -12,7 +12,7 @@ namespace gqa {
 
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 // grid (Hq, B), one thread per output channel; partitions are folded kUnroll
 // at a time with independent loads and an online log-sum-exp.
