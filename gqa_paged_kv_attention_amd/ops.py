@@ -182,12 +182,40 @@ def _call(fn: str, status: int):
         raise GqaError(fn, status, lib.gqa_status_string(status).decode())
 
 
+class BoundCall:
+    """One library call with its arguments checked and marshalled once.
+
+    Calling it re-issues the same C call (same tensors, workspace, output and
+    stream) with no per-call Python work beyond the ctypes call itself, for
+    loops that repeat a step on fixed buffers (the binding's checks cost about
+    10 us of host time per call).  The tensors are kept alive by the object;
+    `out` is the output tensor the call writes."""
+
+    def __init__(self, name, fn, args, keep, out):
+        self.name, self._fn, self._args, self._keep, self.out = name, fn, args, keep, out
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            _call(self.name, status)
+        return self.out
+
+
+def _issue(name, fn, args, bind, keep, out):
+    if bind:
+        return BoundCall(name, fn, args, keep, out)
+    _call(name, fn(*args))
+    return out
+
+
 # --------------------------------------------------------------------------
 # public API (same names as the C ABI)
 # --------------------------------------------------------------------------
 
-def reshape_and_cache(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc, stream=None):
-    """Write new keys/values ``[T, Hkv, d]`` into the paged caches (in place)."""
+def reshape_and_cache(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc, stream=None,
+                      bind=False):
+    """Write new keys/values ``[T, Hkv, d]`` into the paged caches (in place).  With ``bind`` a
+    BoundCall is returned instead."""
     nb, hkv, bs, d = _check_caches(key_cache, value_cache)
     if key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
         _shape_error("key", key.shape, ("tokens", hkv, d))
@@ -201,9 +229,10 @@ def reshape_and_cache(key, value, key_cache, value_cache, block_tables, seq_lens
         raise TypeError("key/value and caches must share a dtype")
     dims = make_dims(num_seqs=seq_lens.shape[0], num_heads=key_cache.shape[1], key_cache=key_cache,
                      block_tables=block_tables, q_dtype=key.dtype, out_dtype=key.dtype)
-    _call("reshape_and_cache", lib.reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
-                                                     _ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc),
-                                                     key.shape[0], dims, _stream(stream)))
+    args = (_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+            _ptr(query_start_loc), key.shape[0], dims, _stream(stream))
+    return _issue("reshape_and_cache", lib.reshape_and_cache, args, bind,
+                  (key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc), None)
 
 
 def decode_workspace_size(dims: Dims, max_seq_len: int, partition_size: int) -> int:
@@ -226,8 +255,9 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
-                     partition_size: int = 0, out=None, out_dtype=None, workspace=None, stream=None):
-    """Decode attention: ``query [B, Hq, d]`` -> ``out [B, Hq, d]``."""
+                     partition_size: int = 0, out=None, out_dtype=None, workspace=None, stream=None, bind=False):
+    """Decode attention: ``query [B, Hq, d]`` -> ``out [B, Hq, d]``.  With ``bind`` the
+    call is not issued: a BoundCall that issues it is returned."""
     _, hkv, _, d = _check_caches(key_cache, value_cache)
     _check_query(query, hkv, d)
     B, Hq, d = query.shape
@@ -243,11 +273,10 @@ def paged_gqa_decode(query, key_cache, value_cache, block_tables, seq_lens, max_
                      out_dtype=out_dtype)
     nbytes = int(lib.paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
     ws, wsb = _workspace(nbytes, query.device, workspace)
-    _call("paged_gqa_decode", lib.paged_gqa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                                                   _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
-                                                   float(scale), int(partition_size), _ptr(ws), wsb,
-                                                   _stream(stream)))
-    return out
+    args = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+            int(max_seq_len), dims, float(scale), int(partition_size), _ptr(ws), wsb, _stream(stream))
+    return _issue("paged_gqa_decode", lib.paged_gqa_decode, args, bind,
+                  (query, key_cache, value_cache, block_tables, seq_lens, ws), out)
 
 
 def paged_gqa_decode_noalloc(query, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
@@ -277,10 +306,10 @@ def paged_gqa_decode_noalloc(query, key_cache, value_cache, block_tables, seq_le
 
 def paged_gqa_decode_append(query, key, value, key_cache, value_cache, block_tables, seq_lens, max_seq_len: int,
                             scale: float, partition_size: int = 0, out=None, out_dtype=None, workspace=None,
-                            stream=None):
+                            stream=None, bind=False):
     """One decode step with the cache write fused: ``key``/``value [B, Hkv, d]`` (each sequence's new
     token, at position seq_lens[b] - 1) go into the caches, and ``query [B, Hq, d]`` -> ``out [B, Hq, d]``
-    attends over all seq_lens[b] tokens."""
+    attends over all seq_lens[b] tokens.  With ``bind`` a BoundCall is returned instead."""
     _, hkv, _, d = _check_caches(key_cache, value_cache)
     _check_query(query, hkv, d)
     B, Hq, d = query.shape
@@ -298,11 +327,11 @@ def paged_gqa_decode_append(query, key, value, key_cache, value_cache, block_tab
                      out_dtype=out_dtype)
     nbytes = int(lib.paged_gqa_decode_workspace_size(dims, int(max_seq_len), int(partition_size)))
     ws, wsb = _workspace(nbytes, query.device, workspace)
-    _call("paged_gqa_decode_append",
-          lib.paged_gqa_decode_append(_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache),
-                                      _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims,
-                                      float(scale), int(partition_size), _ptr(ws), wsb, _stream(stream)))
-    return out
+    args = (_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+            _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), dims, float(scale), int(partition_size), _ptr(ws),
+            wsb, _stream(stream))
+    return _issue("paged_gqa_decode_append", lib.paged_gqa_decode_append, args, bind,
+                  (query, key, value, key_cache, value_cache, block_tables, seq_lens, ws), out)
 
 
 def splitk_lse_reduce(partial_out, partial_lse, seq_lens, partition_size: int, *, num_kv_heads: int,
@@ -343,8 +372,9 @@ def splitk_lse_reduce(partial_out, partial_lse, seq_lens, partition_size: int, *
 
 def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
                                  max_query_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
-                                 out=None, out_dtype=None, workspace=None, stream=None):
-    """Mixed prefill-chunk + decode attention: ``query [T, Hq, d]`` -> ``out [T, Hq, d]``."""
+                                 out=None, out_dtype=None, workspace=None, stream=None, bind=False):
+    """Mixed prefill-chunk + decode attention: ``query [T, Hq, d]`` -> ``out [T, Hq, d]``.  With
+    ``bind`` a BoundCall is returned instead."""
     _, hkv, _, d = _check_caches(key_cache, value_cache)
     _check_query(query, hkv, d)
     T, Hq, d = query.shape
@@ -360,12 +390,11 @@ def chunked_prefill_paged_decode(query, key_cache, value_cache, block_tables, se
                      q_dtype=query.dtype, out_dtype=out_dtype)
     nbytes = int(lib.chunked_prefill_paged_decode_workspace_size(dims, T, int(max_seq_len), int(partition_size)))
     ws, wsb = _workspace(nbytes, query.device, workspace)
-    _call("chunked_prefill_paged_decode",
-          lib.chunked_prefill_paged_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                                           _ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc), T,
-                                           int(max_query_len), int(max_seq_len), dims, float(scale),
-                                           int(partition_size), _ptr(ws), wsb, _stream(stream)))
-    return out
+    args = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+            _ptr(query_start_loc), T, int(max_query_len), int(max_seq_len), dims, float(scale), int(partition_size),
+            _ptr(ws), wsb, _stream(stream))
+    return _issue("chunked_prefill_paged_decode", lib.chunked_prefill_paged_decode, args, bind,
+                  (query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, ws), out)
 
 
 def cross_workspace_size(dims: Dims, num_tokens: int, max_encoder_len: int, partition_size: int) -> int:

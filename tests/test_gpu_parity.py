@@ -501,3 +501,39 @@ def test_full_longctx_splitk(partition):
     """Both splits the benchmark times: 512-token partitions and the library's."""
     bt = wl.longctx_splitk(seed=5)
     assert_parity(decode_step(bt, partition), full_size.longctx(), bt.dtype, bt.describe())
+
+
+def test_bound_calls_match_direct_calls():
+    """A BoundCall re-issues the very call the binding makes: same outputs, bit for bit, on every re-issue."""
+    bt = wl.llama31_8b_decode(seed=21, num_seqs=12, ctx_lo=200, ctx_hi=1500)
+    dev = DeviceBatch(bt)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device="cuda")
+    direct = ops.paged_gqa_decode(dev.query, dev.key_cache, dev.value_cache, dev.block_tables, dev.seq_lens,
+                                  bt.max_seq_len, bt.scale, partition_size=64, workspace=ws).clone()
+    bound = ops.paged_gqa_decode(dev.query, dev.key_cache, dev.value_cache, dev.block_tables, dev.seq_lens,
+                                 bt.max_seq_len, bt.scale, partition_size=64, out=out, workspace=ws, bind=True)
+    assert isinstance(bound, ops.BoundCall)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        assert bound() is out
+        torch.cuda.synchronize()
+        assert torch.equal(out, direct)
+
+    # The fused step: the bound call writes the caches and the output like the direct call.
+    a, b = DeviceBatch(bt), DeviceBatch(bt)
+    ref = ops.paged_gqa_decode_append(a.query, a.new_key, a.new_value, a.key_cache, a.value_cache, a.block_tables,
+                                      a.seq_lens, bt.max_seq_len, bt.scale)
+    step = ops.paged_gqa_decode_append(b.query, b.new_key, b.new_value, b.key_cache, b.value_cache, b.block_tables,
+                                       b.seq_lens, bt.max_seq_len, bt.scale, bind=True)
+    got = step()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(a.key_cache, b.key_cache) and torch.equal(a.value_cache, b.value_cache)
+
+    # A failing bound call raises like the direct call.
+    bad = ops.paged_gqa_decode(dev.query, dev.key_cache, dev.value_cache, dev.block_tables, dev.seq_lens,
+                               bt.max_seq_len, bt.scale, partition_size=64, out=out,
+                               workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"), bind=True)
+    with pytest.raises(ops.GqaError):
+        bad()
