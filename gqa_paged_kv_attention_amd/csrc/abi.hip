@@ -1,6 +1,7 @@
 // C ABI of libgqa_paged.so: host-side validation of scalar arguments, grid
 // sizing and kernel dispatch.  No allocation, no synchronisation, no state.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -74,6 +75,40 @@ bool use_stream(const gqa_dims& d, int32_t partition_size) {
   return (long long)d.num_seqs * d.num_kv_heads < 2 * resident_groups;
 }
 
+// Compute units of the current device (cached per device; 256 without one).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// The partition size the library picks (partition_size == 0) when the
+// balanced decode does not run (G > 16, or many units): one partition per
+// sequence, except when the batch has fewer (sequence, kv head) units than
+// the device has compute units.  Then sequences are cut into partitions of at
+// least kMinPickedPartition tokens, enough of them for about two work-groups
+// per compute unit: with G = 32 a partition's partial (32 rows x D fp32) is as
+// large as the K and V of 32 tokens, and shorter partitions lost (MQA, 128
+// sequences of U{32..1024} tokens: 23.6 us with one partition per sequence,
+// 20.6 us at 512 tokens, 26.8 us at 256, 38.6 us at 128).
+constexpr int kMinPickedPartition = 512;
+int32_t picked_partition(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
+  if (partition_size != 0 || d.num_seqs == 0) return partition_size;
+  const long long units = (long long)d.num_seqs * d.num_kv_heads;
+  const long long cus = device_cus();
+  if (units >= cus) return 0;
+  const long long want = (2 * cus + units - 1) / units;                // partitions per sequence
+  const long long p = std::max<long long>(kMinPickedPartition, (max_seq_len + want - 1) / want);
+  const long long psize = (p + kTileTokens - 1) / kTileTokens * kTileTokens;
+  return psize < max_seq_len ? (int32_t)psize : 0;
+}
+
 // Fixed partitions (partition_size > 0) with G <= 16 run the partitioned
 // balanced decode: persistent waves walk whole partitions back to back, their
 // load pipeline running across partition boundaries, instead of one
@@ -110,7 +145,7 @@ int device_workers(const gqa_dims& d) {
 size_t decode_workspace(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
   if (use_stream(d, partition_size)) return stream_bytes(d, device_workers(d));
   int psize = 0, nparts = 0;
-  if (!partitioning(max_seq_len, partition_size, &psize, &nparts)) return 0;
+  if (!partitioning(max_seq_len, picked_partition(d, max_seq_len, partition_size), &psize, &nparts)) return 0;
   return partial_bytes(d, nparts);
 }
 
@@ -206,6 +241,8 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     return status_from(gqa::launch_stream_reduce(a, dims.head_dim, kv_f32, out_f32, stream));
   }
 
+  if (!partitioning(max_seq_len, picked_partition(dims, max_seq_len, partition_size), &psize, &nparts))
+    return GQA_ERR_INVALID_ARG;
   const size_t need = partial_bytes(dims, nparts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
   if (dims.num_seqs == 0) return GQA_OK;
@@ -400,6 +437,8 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
   {
     int ps = 0, np = 0;
     if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
+    if (!partitioning(max_seq_len, picked_partition(dims, max_seq_len, partition_size), &ps, &np))
+      return GQA_ERR_INVALID_ARG;
     if (use_stream(dims, partition_size)) {
       if (workspace == nullptr || workspace_bytes < stream_bytes(dims, gqa::kStreamWorkersPerGroup))
         return GQA_ERR_WORKSPACE;

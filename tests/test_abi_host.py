@@ -70,6 +70,27 @@ def test_page_sizes_accepted(lib, bs):
         WORKSPACE
 
 
+def test_library_partition_pick_for_large_groups(lib):
+    """With partition_size 0 and G = 32, a batch of fewer (sequence, kv head) units than the
+    device's 256 compute units is cut into partitions of at least 512 tokens (about two
+    work-groups per compute unit); otherwise each sequence is one partition."""
+    al = lambda x: (x + 255) // 256 * 256
+    mqa = dims(num_seqs=128, num_kv_heads=1, max_blocks_per_seq=64)
+    rows = 128 * 32 * 2                     # two 512-token partitions of max_seq_len 1024
+    assert lib.paged_gqa_decode_workspace_size(mqa, 1024, 0) == al(rows * 128 * 4) + al(rows * 4)
+    assert lib.paged_gqa_decode_workspace_size(mqa, 512, 0) == 0      # already one 512-token partition
+    # 4 units: up to 128 partitions of at least 512 tokens
+    few = dims(num_seqs=4, num_kv_heads=1, max_blocks_per_seq=1024)
+    rows = 4 * 32 * 32                      # 16384 / 512
+    assert lib.paged_gqa_decode_workspace_size(few, 16384, 0) == al(rows * 128 * 4) + al(rows * 4)
+    # 256 units fill the device: one partition per sequence
+    g2 = dims(num_seqs=128, num_kv_heads=1 * 2, num_heads=64, max_blocks_per_seq=64)
+    assert lib.paged_gqa_decode_workspace_size(g2, 1024, 0) == 0
+    # an explicit partition size is kept
+    rows = 128 * 32 * 4
+    assert lib.paged_gqa_decode_workspace_size(mqa, 1024, 256) == al(rows * 128 * 4) + al(rows * 4)
+
+
 def test_decode_rejects_null_pointer_and_bad_partition(lib):
     assert decode(lib, dims(), ptr=None) == INVALID
     assert decode(lib, dims(), partition=48) == INVALID        # not a multiple of 32
