@@ -109,6 +109,22 @@ int32_t picked_partition(const gqa_dims& d, int32_t max_seq_len, int32_t partiti
   return psize < max_seq_len ? (int32_t)psize : 0;
 }
 
+// Cache policy of the decode's K/V loads: the non-temporal hint when the
+// K/V the call can read, min(num_seqs x max_seq_len, the whole page pool)
+// tokens, exceeds twice the 256 MB last-level cache of the device, so that
+// the stream of pages that will not be reused before they are evicted does
+// not evict what is; plain loads below that, which leave a batch that fits
+// in that cache for the next call on the same batch to find there.  The
+// bound overestimates what is read (up to 2x for lengths spread evenly up to
+// max_seq_len), hence twice the cache.
+constexpr double kStreamKvBytes = 512.0 * (1 << 20);
+bool stream_kv(const gqa_dims& d, int32_t max_seq_len) {
+  const double per_token = 2.0 * d.num_kv_heads * d.head_dim * (d.kv_dtype == GQA_F32 ? 4 : 2);
+  const double upper = (double)d.num_seqs * std::max(max_seq_len, 0) * per_token;
+  const double pool = (double)d.num_blocks * d.block_size * per_token;
+  return std::min(upper, pool) > kStreamKvBytes;
+}
+
 // Fixed partitions (partition_size > 0) with G <= 16 run the partitioned
 // balanced decode: persistent waves walk whole partitions back to back, their
 // load pipeline running across partition boundaries, instead of one
@@ -236,7 +252,8 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     a.num_workers = workers;
     a.block_size = dims.block_size;
     a.scale_log2 = scale_log2;
-    hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, stream);
+    hipError_t e = gqa::launch_stream_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32,
+                                             stream_kv(dims, max_seq_len), stream);
     if (e != hipSuccess) return GQA_ERR_LAUNCH;
     return status_from(gqa::launch_stream_reduce(a, dims.head_dim, kv_f32, out_f32, stream));
   }
@@ -290,9 +307,11 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     sp.d = a;
     sp.num_seqs = dims.num_seqs;
     sp.num_workers = gqa::partition_workers(dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs);
-    e = gqa::launch_stream_partition(sp, dims.head_dim, dims.block_size, kv_f32, out_f32, stream);
+    e = gqa::launch_stream_partition(sp, dims.head_dim, dims.block_size, kv_f32, out_f32, stream_kv(dims, max_seq_len),
+                                     stream);
   } else {
-    e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, stream);
+    e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs,
+                           stream_kv(dims, max_seq_len), stream);
   }
   if (e != hipSuccess || nparts <= 1) return status_from(e);
   gqa::ReduceArgs r;

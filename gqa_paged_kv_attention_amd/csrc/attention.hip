@@ -633,25 +633,29 @@ hipError_t decode_dispatch_nt(const DecodeArgs& a, int num_seqs, hipStream_t str
   return launch_kernel(decode_kernel<Tile, D, 2, OutT>, grid, dim3(kThreads), 0, stream, a);
 }
 
-// Call f(Tile type tag, head dim tag) for the cache dtype, head_dim and page size.
+// Call f(Tile type tag, head dim tag) for the cache dtype, head_dim and page
+// size; bf16 tiles with non-temporal K/V loads when `stream_kv`.
 template <class F>
-auto with_tile(int D, int block_size, bool kv_f32, F f) {
+auto with_tile(int D, int block_size, bool kv_f32, bool stream_kv, F f) {
   return with_block_size(block_size, [&](auto bs) {
     constexpr int BS = decltype(bs)::value;
     if (kv_f32)
       return D == 64 ? f(TileF32<64, BS>{}, std::integral_constant<int, 64>{})
                      : f(TileF32<128, BS>{}, std::integral_constant<int, 128>{});
-    return D == 64 ? f(TileBF16<64, BS>{}, std::integral_constant<int, 64>{})
-                   : f(TileBF16<128, BS>{}, std::integral_constant<int, 128>{});
+    if (stream_kv)
+      return D == 64 ? f(TileBF16<64, BS, true>{}, std::integral_constant<int, 64>{})
+                     : f(TileBF16<128, BS, true>{}, std::integral_constant<int, 128>{});
+    return D == 64 ? f(TileBF16<64, BS, false>{}, std::integral_constant<int, 64>{})
+                   : f(TileBF16<128, BS, false>{}, std::integral_constant<int, 128>{});
   });
 }
 
 // Resolve the stream-decode instantiation for (D, page size, dtype, out dtype,
 // group) and hand it to `f`.
 template <class F>
-auto with_stream_kernel(int D, int block_size, bool kv_f32, bool out_f32, int group, F f) {
+auto with_stream_kernel(int D, int block_size, bool kv_f32, bool out_f32, int group, bool stream_kv, F f) {
   typedef void (*K)(StreamArgs);
-  K k = with_tile(D, block_size, kv_f32, [&](auto tile, auto dd) {
+  K k = with_tile(D, block_size, kv_f32, stream_kv, [&](auto tile, auto dd) {
     typedef decltype(tile) Tile;
     constexpr int DD = decltype(dd)::value;
     if (group <= 16)
@@ -664,8 +668,8 @@ auto with_stream_kernel(int D, int block_size, bool kv_f32, bool out_f32, int gr
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs,
-                         hipStream_t stream) {
-  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+                         bool stream_kv, hipStream_t stream) {
+  return with_tile(head_dim, block_size, kv_f32, stream_kv, [&](auto tile, auto dd) {
     typedef decltype(tile) Tile;
     constexpr int DD = decltype(dd)::value;
     return out_f32 ? decode_dispatch_nt<Tile, DD, float>(a, num_seqs, stream)
@@ -677,7 +681,8 @@ int prefill_rows_per_group() { return PrefillShape<kPrefillNTW>::kRowsPerGroup; 
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
                           int grid_groups, hipStream_t stream) {
-  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+  // chunks re-read their keys across row tiles: plain loads
+  return with_tile(head_dim, block_size, kv_f32, false, [&](auto tile, auto dd) {
     typedef decltype(tile) Tile;
     constexpr int DD = decltype(dd)::value;
     if (out_f32)
@@ -721,16 +726,19 @@ int resident_workers(const void* kernel, size_t lds_bytes) {
   return workers;
 }
 
+// Both cache-policy instantiations of a kernel use the same registers and LDS
+// (they differ only in the hint bits of the loads), so the counts come from
+// the streaming one.
 int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs) {
-  void (*kernel)(StreamArgs) =
-      with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, [](void (*k)(StreamArgs)) { return k; });
+  void (*kernel)(StreamArgs) = with_stream_kernel(head_dim, block_size, kv_f32, out_f32, group, true,
+                                                  [](void (*k)(StreamArgs)) { return k; });
   return resident_workers(reinterpret_cast<const void*>(kernel), (size_t)(2 * num_seqs + 1) * sizeof(int));
 }
 
 // The partitioned balanced decode's instantiation for (D, page size, dtype, out dtype).
-void (*partition_kernel(int head_dim, int block_size, bool kv_f32, bool out_f32))(StreamPartArgs) {
+void (*partition_kernel(int head_dim, int block_size, bool kv_f32, bool out_f32, bool stream_kv))(StreamPartArgs) {
   typedef void (*K)(StreamPartArgs);
-  return with_tile(head_dim, block_size, kv_f32, [&](auto tile, auto dd) {
+  return with_tile(head_dim, block_size, kv_f32, stream_kv, [&](auto tile, auto dd) {
     typedef decltype(tile) Tile;
     constexpr int DD = decltype(dd)::value;
     return out_f32 ? (K)stream_partition_kernel<Tile, DD, float> : (K)stream_partition_kernel<Tile, DD, uint16_t>;
@@ -738,22 +746,22 @@ void (*partition_kernel(int head_dim, int block_size, bool kv_f32, bool out_f32)
 }
 
 int partition_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs) {
-  return resident_workers(reinterpret_cast<const void*>(partition_kernel(head_dim, block_size, kv_f32, out_f32)),
+  return resident_workers(reinterpret_cast<const void*>(partition_kernel(head_dim, block_size, kv_f32, out_f32, true)),
                           (size_t)(2 * num_seqs + 1) * sizeof(int));
 }
 
 hipError_t launch_stream_partition(const StreamPartArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
-                                   hipStream_t stream) {
+                                   bool stream_kv, hipStream_t stream) {
   const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
-  return launch_kernel(partition_kernel(head_dim, block_size, kv_f32, out_f32), dim3(a.num_workers / kWaves),
+  return launch_kernel(partition_kernel(head_dim, block_size, kv_f32, out_f32, stream_kv), dim3(a.num_workers / kWaves),
                        dim3(kThreads), lds, stream, a);
 }
 
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
-                                hipStream_t stream) {
+                                bool stream_kv, hipStream_t stream) {
   const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
   const dim3 grid(a.num_workers / kWaves), block(kThreads);
-  return with_stream_kernel(head_dim, block_size, kv_f32, out_f32, a.group, [&](void (*k)(StreamArgs)) {
+  return with_stream_kernel(head_dim, block_size, kv_f32, out_f32, a.group, stream_kv, [&](void (*k)(StreamArgs)) {
     return launch_kernel(k, grid, block, lds, stream, a);
   });
 }

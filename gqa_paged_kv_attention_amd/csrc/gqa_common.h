@@ -190,14 +190,22 @@ __device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_b
 //    offsets 8 (q & 1) ..), a contiguous 16-byte run of the channel-major page.
 //  - P is fed as a hi/lo pair of bf16 (p = hi + lo to ~2^-16 relative), so the
 //    P.V product keeps fp32-grade weights.
-template <int D, int BS>
+//  - Stream: K/V loads carry the non-temporal hint (read once, do not keep
+//    them in L2 / the last-level cache).  The host picks it per call from the
+//    batch's K/V footprint: for a batch far larger than the last-level cache
+//    the hint keeps the stream from evicting what is reused (Llama-3.1-8B
+//    decode batch, 634 MB: 123 -> 111 us); a batch that fits is read again
+//    from that cache by the next call on it, which the hint would forgo
+//    (Llama-2-7B sweep with Hkv = 8, 273 MB: 48 us plain, 57 us with it).
+template <int D, int BS, bool Stream = false>
 struct TileBF16 {
   static constexpr int kBS = BS;
-  // Value loads stream (non-temporal) unless one 128-byte line of a channel
-  // holds both tiles of a pair (64-token pages): the second tile's half of
-  // the line must still be in L2 when it is asked for (with the hint, 64-token
-  // pages went from 129 to 152 us on the Llama-3.1-8B decode batch).
-  static constexpr bool kStreamV = BS * 2 <= 64;
+  // Value loads stream only when one 128-byte line of a channel does not hold
+  // both tiles of a pair (64-token pages): the second tile's half of the line
+  // must still be in L2 when it is asked for (with the hint, 64-token pages
+  // went from 129 to 152 us on the Llama-3.1-8B decode batch).
+  static constexpr bool kStreamK = Stream;
+  static constexpr bool kStreamV = Stream && BS * 2 <= 64;
   static constexpr bool kPipelined = true;  // double-buffered tile loop
   static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
   static constexpr int DT = D / 16;   // 16-channel blocks of the output
@@ -218,7 +226,7 @@ struct TileBF16 {
       const int slot = (m & 3) + 8 * ((m >> 2) & 1) + 4 * s;
       const elem_t* row = pg + slot * D + 8 * q;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) k.v[s][c] = ld16_stream(row + 32 * c);
+      for (int c = 0; c < KC; ++c) k.v[s][c] = kStreamK ? ld16_stream(row + 32 * c) : ld16(row + 32 * c);
     }
   }
 

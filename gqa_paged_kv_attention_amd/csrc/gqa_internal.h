@@ -134,17 +134,19 @@ struct CacheWriteArgs {
 
 // kv_f32 / out_f32 select fp32 (true) or bf16 (false) storage; block_size is
 // the page size in tokens (16, 32 or 64).
+// stream_kv: bf16 K/V loads with the non-temporal hint (for batches whose K/V
+// is far larger than the last-level cache).
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs,
-                         hipStream_t stream);
+                         bool stream_kv, hipStream_t stream);
 // Workers (4 per work-group) that fill the device at full occupancy.
 int stream_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int group, int num_seqs);
 hipError_t launch_stream_decode(const StreamArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
-                                hipStream_t stream);
+                                bool stream_kv, hipStream_t stream);
 hipError_t launch_stream_reduce(const StreamArgs& a, int head_dim, bool kv_f32, bool out_f32, hipStream_t stream);
 // Resident waves of the partitioned balanced decode, and its launch (a.num_workers / 4 work-groups).
 int partition_workers(int head_dim, int block_size, bool kv_f32, bool out_f32, int num_seqs);
 hipError_t launch_stream_partition(const StreamPartArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
-                                   hipStream_t stream);
+                                   bool stream_kv, hipStream_t stream);
 // Rows per prefill work-group (depends only on the build).
 int prefill_rows_per_group();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool kv_f32, bool out_f32,
