@@ -60,19 +60,37 @@ int status_from(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH
 
 int device_workers(const gqa_dims& d);
 
-// partition_size == 0 picks the decomposition.  The balanced (stream) decode
-// pays a merge kernel and per-segment restarts, which only win when the batch
-// has too few (sequence, kv head) units to balance itself over the device's
-// resident work-groups; with many units, or G > 16 (a segment then weighs as
-// much as a tile), one work-group per unit is faster.  The stream kernel also
-// needs the batch to fit its LDS table and the tile count to fit in 32 bits.
-bool use_stream(const gqa_dims& d, int32_t partition_size) {
+// partition_size == 0 picks the decomposition: the balanced (stream) decode,
+// or one work-group per (sequence, kv head) unit.  The balanced decode pays a
+// merge kernel, the partials of the units it cuts (G x D fp32 each) and a
+// start per segment; one work-group per unit pays for the longest unit, whose
+// four waves walk max_seq_len / 128 tiles each while shorter units' work-groups
+// sit idle.  So the balanced decode runs when the batch has few units (at most
+// an eighth of the device's resident work-groups) or when the longest sequence
+// is long enough for that imbalance to outweigh the split's costs, a length
+// that grows with G (more partial bytes per cut): max_seq_len > 768 G.
+// Measured (bf16, d = 128, lengths uniform in the ranges; balanced / one
+// work-group per unit, us):
+//   64 seqs x 8 kv heads, 512..4096 tokens, G = 4: 106 / 128 -> balanced
+//   16 x 8, 1024..8192, G = 4: 56 / 84;  16 x 8, 512..4096, G = 4: 34 / 40
+//   2 kv heads x 16 seqs, 2048..4096, G = 16: 32 / 39
+//   128 x 2, 32..1024, G = 16: 28 / 17 -> one per unit
+//   32 x 8, 512..1024, G = 4: 26 / 19;  32 x 8, 1024..2048, G = 4: 40 / 34
+//   32 x 8, 2048..4096, G = 8: 85 / 76;  16 x 8, 1024..2048, G = 8: 28 / 25
+//   64 x 8, 512..1024, G = 4: 40 / 34;  64 x 2, 1024..2048, G = 16: 31 / 26
+// G > 16 never takes it (a cut segment's partial weighs as much as a tile).
+// The stream kernel also needs the batch to fit its LDS table and the tile
+// count to fit in 32 bits.
+bool use_stream(const gqa_dims& d, int32_t partition_size, int32_t max_seq_len) {
   if (partition_size != 0 || d.num_seqs == 0 || d.num_seqs > gqa::kMaxStreamSeqs) return false;
-  if (d.num_heads / d.num_kv_heads > 16) return false;
+  const int G = d.num_heads / d.num_kv_heads;
+  if (G > 16) return false;
   const long long tiles_per_seq = ((long long)d.max_blocks_per_seq * d.block_size + kTileTokens - 1) / kTileTokens;
   if ((long long)d.num_seqs * d.num_kv_heads * tiles_per_seq >= (1LL << 31) - 1) return false;
   const long long resident_groups = device_workers(d) / gqa::kStreamWorkersPerGroup;
-  return (long long)d.num_seqs * d.num_kv_heads < 2 * resident_groups;
+  const long long units = (long long)d.num_seqs * d.num_kv_heads;
+  if (units >= 2 * resident_groups) return false;
+  return 8 * units <= resident_groups || (long long)max_seq_len > 768LL * G;
 }
 
 // Compute units of the current device (cached per device; 256 without one).
@@ -89,9 +107,9 @@ int device_cus() {
 }
 
 // The partition size the library picks (partition_size == 0) when the
-// balanced decode does not run (G > 16, or many units): one partition per
-// sequence, except when the batch has fewer (sequence, kv head) units than
-// the device has compute units.  Then sequences are cut into partitions of at
+// balanced decode does not run: one partition per sequence, except for G > 16
+// when the batch has fewer (sequence, kv head) units than the device has
+// compute units.  Then sequences are cut into partitions of at
 // least kMinPickedPartition tokens, enough of them for about two work-groups
 // per compute unit: with G = 32 a partition's partial (32 rows x D fp32) is as
 // large as the K and V of 32 tokens, and shorter partitions lost (MQA, 128
@@ -99,7 +117,7 @@ int device_cus() {
 // 20.6 us at 512 tokens, 26.8 us at 256, 38.6 us at 128).
 constexpr int kMinPickedPartition = 512;
 int32_t picked_partition(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
-  if (partition_size != 0 || d.num_seqs == 0) return partition_size;
+  if (partition_size != 0 || d.num_seqs == 0 || d.num_heads / d.num_kv_heads <= 16) return partition_size;
   const long long units = (long long)d.num_seqs * d.num_kv_heads;
   const long long cus = device_cus();
   if (units >= cus) return 0;
@@ -159,7 +177,7 @@ int device_workers(const gqa_dims& d) {
 }
 
 size_t decode_workspace(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
-  if (use_stream(d, partition_size)) return stream_bytes(d, device_workers(d));
+  if (use_stream(d, partition_size, max_seq_len)) return stream_bytes(d, device_workers(d));
   int psize = 0, nparts = 0;
   if (!partitioning(max_seq_len, picked_partition(d, max_seq_len, partition_size), &psize, &nparts)) return 0;
   return partial_bytes(d, nparts);
@@ -211,7 +229,7 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
   const bool kv_f32 = dims.kv_dtype == GQA_F32, out_f32 = dims.out_dtype == GQA_F32;
   const float scale_log2 = scale * 1.4426950408889634f;
 
-  if (use_stream(dims, partition_size)) {
+  if (use_stream(dims, partition_size, max_seq_len)) {
     if (workspace == nullptr) return GQA_ERR_WORKSPACE;
     // as many workers as the device holds at once, fewer if the workspace is smaller
     int workers = device_workers(dims);
@@ -458,7 +476,7 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     if (!partitioning(max_seq_len, partition_size, &ps, &np)) return GQA_ERR_INVALID_ARG;
     if (!partitioning(max_seq_len, picked_partition(dims, max_seq_len, partition_size), &ps, &np))
       return GQA_ERR_INVALID_ARG;
-    if (use_stream(dims, partition_size)) {
+    if (use_stream(dims, partition_size, max_seq_len)) {
       if (workspace == nullptr || workspace_bytes < stream_bytes(dims, gqa::kStreamWorkersPerGroup))
         return GQA_ERR_WORKSPACE;
     } else {
