@@ -38,12 +38,12 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 
 # HBM traffic of one step call (paged_gqa_decode_append on this workload, both
 # of its kernels), from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB
-# per dispatch) over `bench.py --steps 20 --warmup 5 --no-mixed
-# --no-cpu-baseline --no-comparisons` (and no other leg), each scaled by what the same counter reads for the
-# 512 MiB copy of `bench.py --copy-calibration`.  Valid only for the decode
-# sources it was measured on (their SHA-256 below); otherwise reported as null.
+# per dispatch) over `bench.py --profile-leg decode_step --profile-calls 20`, each
+# scaled by what the same counter reads for the 512 MiB copy of
+# `bench.py --copy-calibration`.  Valid only for the decode sources it was
+# measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "a4c9c579bb51148e2a11858c07847a832d6afc625ec6468c9c93bfc6c5116258", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 648800525, "write_bytes_per_call": 8563405, "hbm_bytes_per_call": 657363930, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "55be24eb694366faa8696f7dd8e0d9159560e66aaf61d5666154296aed0e67f0", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669624291, "write_bytes_per_call": 8541798, "hbm_bytes_per_call": 678166089, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
