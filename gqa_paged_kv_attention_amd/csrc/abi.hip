@@ -108,16 +108,21 @@ int device_cus() {
 
 // The partition size the library picks (partition_size == 0) when the
 // balanced decode does not run: one partition per sequence, except for G > 16
-// when the batch has fewer (sequence, kv head) units than the device has
-// compute units.  Then sequences are cut into partitions of at
-// least kMinPickedPartition tokens, enough of them for about two work-groups
-// per compute unit: with G = 32 a partition's partial (32 rows x D fp32) is as
-// large as the K and V of 32 tokens, and shorter partitions lost (MQA, 128
-// sequences of U{32..1024} tokens: 23.6 us with one partition per sequence,
-// 20.6 us at 512 tokens, 26.8 us at 256, 38.6 us at 128).
+// over K/V beyond the last-level cache (smaller K/V runs each kv head's query
+// heads as two 16-row units instead, see run_decode) when the batch has fewer
+// (sequence, kv head) units than the device has compute units.  Then
+// sequences are cut into partitions of at least kMinPickedPartition tokens,
+// enough of them for about two work-groups per compute unit: with G = 32 a
+// partition's partial (32 rows x D fp32) is as large as the K and V of 32
+// tokens, and shorter partitions lost (MQA, 128 sequences of U{32..1024}
+// tokens, before the 16-row units: 23.6 us with one partition per sequence,
+// 20.6 us at 512 tokens, 26.8 us at 256, 38.6 us at 128; with the 16-row
+// units, 16.8 us unsplit and 21.4 us at 512 tokens).
 constexpr int kMinPickedPartition = 512;
+bool stream_kv(const gqa_dims& d, int32_t max_seq_len);
 int32_t picked_partition(const gqa_dims& d, int32_t max_seq_len, int32_t partition_size) {
   if (partition_size != 0 || d.num_seqs == 0 || d.num_heads / d.num_kv_heads <= 16) return partition_size;
+  if (!stream_kv(d, max_seq_len)) return 0;
   const long long units = (long long)d.num_seqs * d.num_kv_heads;
   const long long cus = device_cus();
   if (units >= cus) return 0;
@@ -328,8 +333,16 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
     e = gqa::launch_stream_partition(sp, dims.head_dim, dims.block_size, kv_f32, out_f32, stream_kv(dims, max_seq_len),
                                      stream);
   } else {
-    e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs,
-                           stream_kv(dims, max_seq_len), stream);
+    // G = 32 over K/V that the last-level cache holds: each kv head's query heads run as two
+    // units of 16 rows (the 16-row kernel, twice the work-groups); the second unit to read a
+    // page finds it in the cache.
+    const bool skv = stream_kv(dims, max_seq_len);
+    if (a.group > 16 && !skv) {
+      a.kv_split = 2;
+      a.group /= 2;
+      a.num_kv_heads *= 2;
+    }
+    e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, skv, stream);
   }
   if (e != hipSuccess || nparts <= 1) return status_from(e);
   gqa::ReduceArgs r;

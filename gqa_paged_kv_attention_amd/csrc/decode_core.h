@@ -277,13 +277,14 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
     const int wb = tile0 + w * wper + min(w, wextra);
     const int we = wb + wper + (w < wextra ? 1 : 0);
     run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                           a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, wb, we, 1, a.scale_log2, lane);
+                           a.num_blocks, a.num_kv_heads / a.kv_split, kv / a.kv_split, L, t1 - 1, wb, we, 1,
+                           a.scale_log2, lane);
   } else {
     // two row blocks per wave (G > 16): tiles round-robin over the waves, which
     // was faster there (MQA, G = 32: 19.4 vs 20.5 us)
     run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                           a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0 + w, tile0 + n_tiles, kWaves,
-                           a.scale_log2, lane);
+                           a.num_blocks, a.num_kv_heads / a.kv_split, kv / a.kv_split, L, t1 - 1, tile0 + w,
+                           tile0 + n_tiles, kWaves, a.scale_log2, lane);
   }
 
   // ---- merge the four waves ----
@@ -381,7 +382,8 @@ __device__ __forceinline__ void decode_wave_partition(const DecodeArgs& a, int p
   WaveState<Tile, NT> st;
   st.reset();
   run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
-                         a.num_blocks, a.num_kv_heads, kv, L, t1 - 1, tile0, tile0 + n_tiles, 1, a.scale_log2, lane);
+                         a.num_blocks, a.num_kv_heads / a.kv_split, kv / a.kv_split, L, t1 - 1, tile0, tile0 + n_tiles,
+                         1, a.scale_log2, lane);
 
   const size_t head0 = (size_t)b * a.num_heads + kv * G;
 #pragma unroll

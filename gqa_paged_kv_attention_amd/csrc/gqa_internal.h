@@ -37,6 +37,10 @@ struct DecodeArgs {
   int partition_size;               // tokens per partition, multiple of 32
   int max_partitions;
   float scale_log2;                 // scale * log2(e)
+  // 1, or 2 when each kv head's query heads run as two units of `group` rows:
+  // num_kv_heads and the kv index then count those units, and the cache's kv
+  // head is kv / kv_split of num_kv_heads / kv_split.
+  int kv_split = 1;
 };
 
 // Balanced ("stream") decode: persistent waves, each owning an equal slice of

@@ -71,23 +71,29 @@ def test_page_sizes_accepted(lib, bs):
 
 
 def test_library_partition_pick_for_large_groups(lib):
-    """With partition_size 0 and G = 32, a batch of fewer (sequence, kv head) units than the
-    device's 256 compute units is cut into partitions of at least 512 tokens (about two
-    work-groups per compute unit); otherwise each sequence is one partition."""
+    """With partition_size 0 and G = 32 over K/V beyond twice the 256 MB last-level cache, a
+    batch of fewer (sequence, kv head) units than the device's 256 compute units is cut into
+    partitions of at least 512 tokens (about two work-groups per compute unit).  Smaller K/V
+    runs the 16-row units unsplit, and so does a batch that fills the device."""
     al = lambda x: (x + 255) // 256 * 256
-    mqa = dims(num_seqs=128, num_kv_heads=1, max_blocks_per_seq=64)
-    rows = 128 * 32 * 2                     # two 512-token partitions of max_seq_len 1024
-    assert lib.paged_gqa_decode_workspace_size(mqa, 1024, 0) == al(rows * 128 * 4) + al(rows * 4)
-    assert lib.paged_gqa_decode_workspace_size(mqa, 512, 0) == 0      # already one 512-token partition
-    # 4 units: up to 128 partitions of at least 512 tokens
-    few = dims(num_seqs=4, num_kv_heads=1, max_blocks_per_seq=1024)
-    rows = 4 * 32 * 32                      # 16384 / 512
-    assert lib.paged_gqa_decode_workspace_size(few, 16384, 0) == al(rows * 128 * 4) + al(rows * 4)
+    # 128 units, 16k tokens, a 1 GiB pool: four 4096-token partitions per sequence
+    big = dims(num_seqs=128, num_kv_heads=1, max_blocks_per_seq=1024, num_blocks=131072)
+    rows = 128 * 32 * 4
+    assert lib.paged_gqa_decode_workspace_size(big, 16384, 0) == al(rows * 128 * 4) + al(rows * 4)
+    # 4 units of up to 512k tokens: 128 partitions of 4096 tokens per sequence
+    few = dims(num_seqs=4, num_kv_heads=1, max_blocks_per_seq=32768, num_blocks=131072)
+    rows = 4 * 32 * 128
+    assert lib.paged_gqa_decode_workspace_size(few, 524288, 0) == al(rows * 128 * 4) + al(rows * 4)
+    # 4 units of 16k tokens (33.5 MB of K/V): no partitions
+    assert lib.paged_gqa_decode_workspace_size(few, 16384, 0) == 0
+    # the same batches over a small pool (K/V the cache holds): no partitions
+    assert lib.paged_gqa_decode_workspace_size(dims(num_seqs=128, num_kv_heads=1, max_blocks_per_seq=1024), 16384, 0) == 0
     # 256 units fill the device: one partition per sequence
-    g2 = dims(num_seqs=128, num_kv_heads=1 * 2, num_heads=64, max_blocks_per_seq=64)
-    assert lib.paged_gqa_decode_workspace_size(g2, 1024, 0) == 0
+    g2 = dims(num_seqs=128, num_kv_heads=2, num_heads=64, max_blocks_per_seq=1024, num_blocks=131072)
+    assert lib.paged_gqa_decode_workspace_size(g2, 16384, 0) == 0
     # an explicit partition size is kept
     rows = 128 * 32 * 4
+    mqa = dims(num_seqs=128, num_kv_heads=1, max_blocks_per_seq=64)
     assert lib.paged_gqa_decode_workspace_size(mqa, 1024, 256) == al(rows * 128 * 4) + al(rows * 4)
 
 
