@@ -151,20 +151,25 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Page id through the block table, clamped into the pool so that a corrupt
-// entry can give a wrong answer but never an out-of-bounds read.  The row and
-// index are wave-uniform (every lane of a wave walks the same tile), so the
-// entry is read with a scalar load through the constant address space: a
-// vector load would queue in the compute unit's vector memory path behind the
-// K/V loads of the other waves there, and the next tile's K/V loads cannot be
-// issued before it returns (at kernel start that wait was 5-20 us per wave).
-// The block table is not written while a kernel runs.
-__device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_blocks) {
+// Entry idx of a wave-uniform int32 row (a block-table row: every lane of a
+// wave walks the same tile), read with a scalar load through the constant
+// address space.  A vector load would queue in the compute unit's vector
+// memory path behind the K/V loads of the other waves there, and the next
+// tile's K/V loads cannot be issued before it returns (at the decode's start
+// that wait was 5-20 us per wave).  The tables are not written while a kernel
+// runs.
+__device__ __forceinline__ int scalar_entry(const int32_t* row_ptr, int idx) {
   typedef const __attribute__((address_space(4))) int32_t* const_row;
-  const uint64_t row = reinterpret_cast<uint64_t>(bt_row);
+  const uint64_t row = reinterpret_cast<uint64_t>(row_ptr);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)row);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(row >> 32));
-  const int p = reinterpret_cast<const_row>(((uint64_t)hi << 32) | lo)[__builtin_amdgcn_readfirstlane(idx)];
+  return reinterpret_cast<const_row>(((uint64_t)hi << 32) | lo)[__builtin_amdgcn_readfirstlane(idx)];
+}
+
+// Page id through the block table, clamped into the pool so that a corrupt
+// entry can give a wrong answer but never an out-of-bounds read.
+__device__ __forceinline__ int page_at(const int32_t* bt_row, int idx, int num_blocks) {
+  const int p = scalar_entry(bt_row, idx);
   return (unsigned)p < (unsigned)num_blocks ? p : 0;
 }
 

@@ -224,12 +224,13 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   TileCopyPlan<D, NTW, BS> plan;
   plan.init();
   // Raw block-table entries of tile t (clamped to the last tile and page).
-  // They are loaded one iteration before they are used, so that waiting for
-  // them never waits for the K/V loads issued just before.
+  // They are loaded one iteration before they are used, with scalar loads
+  // (the entries are uniform over the work-group), so that waiting for them
+  // never waits for K/V loads in the vector memory path.
   auto fetch_pages = [&](int t, int* raw) {
     const int pg = min(t, n_tiles - 1) * kEntries;
 #pragma unroll
-    for (int j = 0; j < kEntries; ++j) raw[j] = bt[min(pg + j, npages - 1)];
+    for (int j = 0; j < kEntries; ++j) raw[j] = scalar_entry(bt, min(pg + j, npages - 1));
   };
   // 16-token block j of the tile: entry j * 16 / BS, from token j * 16 mod BS of that page
   auto issue = [&](const int* raw, uint4* kr, uint4* vr) {
