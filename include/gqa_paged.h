@@ -86,9 +86,9 @@ typedef struct {
   int32_t block_size;          /* tokens per page: 16, 32 or 64 */
   int32_t num_blocks;          /* pages in each cache */
   int32_t max_blocks_per_seq;  /* row stride of block_tables */
-  gqa_dtype q_dtype;           /* query (and key/value of reshape_and_cache) */
-  gqa_dtype kv_dtype;          /* caches; must equal q_dtype */
-  gqa_dtype out_dtype;         /* output; accumulation is always fp32 */
+  int32_t q_dtype;             /* a gqa_dtype: query (and key/value of reshape_and_cache) */
+  int32_t kv_dtype;            /* a gqa_dtype: caches; must equal q_dtype */
+  int32_t out_dtype;           /* a gqa_dtype: output; accumulation is always fp32 */
 } gqa_dims;
 
 /* Human-readable name of a status code (static storage). */

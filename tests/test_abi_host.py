@@ -2,6 +2,7 @@
 function include/gqa_paged.h declares, and rejects bad scalar arguments with
 status codes before touching the device."""
 import ctypes
+import os
 
 import pytest
 
@@ -12,7 +13,9 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
 @pytest.fixture(scope="module")
 def lib():
-    return ops.load_library()
+    # GQA_TEST_LIB: another build of the same sources (tests/test_abi_sanitized.py runs this
+    # module against the library with its host code built under AddressSanitizer and UBSan)
+    return ops.load_library(os.environ.get("GQA_TEST_LIB", ops.LIB_PATH))
 
 
 def dims(**kw):
