@@ -342,6 +342,10 @@ int run_decode(void* out, const void* query, const void* key_cache, const void* 
       a.group /= 2;
       a.num_kv_heads *= 2;
     }
+    // at most one work-group per compute unit and at most 1024 keys per
+    // work-group: 8 waves, each walking half as many tiles
+    if ((long long)nparts * a.num_kv_heads * dims.num_seqs <= device_cus() && std::min(psize, max_seq_len) <= 1024)
+      a.waves = 8;
     e = gqa::launch_decode(a, dims.head_dim, dims.block_size, kv_f32, out_f32, dims.num_seqs, skv, stream);
   }
   if (e != hipSuccess || nparts <= 1) return status_from(e);

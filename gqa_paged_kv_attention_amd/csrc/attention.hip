@@ -8,17 +8,30 @@
 #include <tuple>
 
 #include "decode_core.h"
+#include "work_map.h"
 
 namespace gqa {
 
 namespace {
 
-// Fixed-partition decode: grid (max_partitions, Hkv, B).
-template <class Tile, int D, int NT, class OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
+// Fixed-partition decode: grid (max_partitions, Hkv, B), W waves per work-group.
+template <class Tile, int D, int NT, class OutT, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<Tile, D, NT>())))
 void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float lds[DecodeMergeLds<D, NT>::kFloats];
-  decode_partition<Tile, D, NT, OutT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  __shared__ __attribute__((aligned(16))) float lds[DecodeMergeLds<D, NT, W>::kFloats];
+  int p = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  if (a.kv_split == 2) {
+    // The two units of a kv head (kv = 2 k and 2 k + 1) read the same pages:
+    // paired_unit gives them ids 8 apart (one XCD, one L2), so that the second
+    // finds the pages the first one fetched.  u enumerates (p, k, b), p fastest.
+    int u, half;
+    paired_unit(p + gridDim.x * (kv + gridDim.y * b), gridDim.x * gridDim.y * gridDim.z, &u, &half);
+    const int hk = gridDim.y / 2;
+    p = u % gridDim.x;
+    kv = 2 * (u / gridDim.x % hk) + half;
+    b = u / gridDim.x / hk;
+  }
+  decode_partition<Tile, D, NT, OutT, W>(a, p, kv, b, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,8 +642,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 template <class Tile, int D, class OutT>
 hipError_t decode_dispatch_nt(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
   dim3 grid(a.max_partitions, a.num_kv_heads, num_seqs);
-  if (a.group <= 16) return launch_kernel(decode_kernel<Tile, D, 1, OutT>, grid, dim3(kThreads), 0, stream, a);
-  return launch_kernel(decode_kernel<Tile, D, 2, OutT>, grid, dim3(kThreads), 0, stream, a);
+  if (a.group > 16) return launch_kernel(decode_kernel<Tile, D, 2, OutT, kWaves>, grid, dim3(kThreads), 0, stream, a);
+  if (a.waves == 2 * kWaves)
+    return launch_kernel(decode_kernel<Tile, D, 1, OutT, 2 * kWaves>, grid, dim3(2 * kThreads), 0, stream, a);
+  return launch_kernel(decode_kernel<Tile, D, 1, OutT, kWaves>, grid, dim3(kThreads), 0, stream, a);
 }
 
 // Call f(Tile type tag, head dim tag) for the cache dtype, head_dim and page

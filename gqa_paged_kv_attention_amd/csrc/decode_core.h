@@ -198,11 +198,11 @@ __device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq, int bloc
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-partition decode: grid (max_partitions, Hkv, B), 4 waves.  Sequence b
-// is split into n = ceil(L / partition_size) partitions of nearly equal length
+// Fixed-partition decode: grid (max_partitions, Hkv, B), W waves (4, or 8 when
+// the grid holds at most one work-group per compute unit).  Sequence b is
+// split into n = ceil(L / partition_size) partitions of nearly equal length
 // (whole 32-token tiles); the work-group owns partition p of one (sequence, kv
-// head), its waves take the partition's tiles round-robin and merge through
-// LDS.  With n == 1 the work-group writes `out`; otherwise it writes the
+// head), its waves share the partition's tiles and merge through LDS.  With n == 1 the work-group writes `out`; otherwise it writes the
 // partition's normalised output and log-sum-exp for the split-K reduce kernel.
 // ---------------------------------------------------------------------------
 // Waves per SIMD the decode kernels are compiled for: two when a double-buffered
@@ -213,12 +213,12 @@ constexpr int decode_waves_per_simd() {
   return (NT == 1 && (sizeof(typename Tile::elem_t) * D <= 256 || !Tile::kPipelined)) ? 2 : 1;
 }
 
-// LDS the merge of the four waves needs (floats): per wave, R row maxima, R
-// row sums and an R x (D + 4) output block.
-template <int D, int NT>
+// LDS the merge of the W waves needs (floats): per wave, R row maxima, R row
+// sums and an R x (D + 4) output block.
+template <int D, int NT, int W = kWaves>
 struct DecodeMergeLds {
   static constexpr int R = NT * 16;
-  static constexpr int kFloats = kWaves * R * (2 + D + 4);
+  static constexpr int kFloats = W * R * (2 + D + 4);
 };
 
 // Where a unit that covers part of a row's keys writes: each row's
@@ -231,17 +231,18 @@ struct UnitOut {
   int slot = 0, slots = 1;
 };
 
-// Partition p of (sequence b, kv head kv), run by the 4 waves of a work-group,
+// Partition p of (sequence b, kv head kv), run by the W waves of a work-group,
 // for query row `row` and seq_lens[b] = seq_len; `lds` holds
-// DecodeMergeLds<D, NT>::kFloats floats.  Partitions cover keys [k_begin, L)
+// DecodeMergeLds<D, NT, W>::kFloats floats.  Partitions cover keys [k_begin, L)
 // (k_begin a multiple of 32).  With `uo`, every partition writes a partial to
 // uo's slots; otherwise a single partition writes `out` and several write
 // a.partial_out / a.partial_lse.
-template <class Tile, int D, int NT, class OutT>
+template <class Tile, int D, int NT, class OutT, int W = kWaves>
 __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, int kv, int b, int row, int seq_len,
                                                     float* lds, int k_begin = 0, const UnitOut* uo = nullptr) {
   constexpr int R = NT * 16;            // padded rows of the group
   const int G = a.group;
+  constexpr int kT = W * kWave;    // threads of the work-group
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, q = lane >> 4;
 
@@ -254,7 +255,7 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
 
   if (nparts == 0) {
     if (p == 0 && !uo)
-      for (int i = threadIdx.x; i < G * D / 4; i += kThreads)
+      for (int i = threadIdx.x; i < G * D / 4; i += kT)
         store4(out + ((size_t)row * a.num_heads + kv * G) * D + 4 * i, zero4());
     return;
   }
@@ -270,10 +271,10 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   WaveState<Tile, NT> st;
   st.reset();
   if constexpr (NT == 1) {
-    // each wave a contiguous quarter of the partition's tiles, walked in pairs
+    // each wave a contiguous share (1 / W) of the partition's tiles, walked in pairs
     // (two tiles per round trip); measured faster than round-robin tiles for
     // G <= 16 (Llama-3.1-8B shapes at 512-token partitions 148.8 -> 141.3 us)
-    const int wper = n_tiles / kWaves, wextra = n_tiles % kWaves;
+    const int wper = n_tiles / W, wextra = n_tiles % W;
     const int wb = tile0 + w * wper + min(w, wextra);
     const int we = wb + wper + (w < wextra ? 1 : 0);
     run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
@@ -284,13 +285,13 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
     // was faster there (MQA, G = 32: 19.4 vs 20.5 us)
     run_tiles<Tile, D, NT>(st, qf, a.key_cache, a.value_cache, a.block_tables + (size_t)b * a.max_blocks_per_seq,
                            a.num_blocks, a.num_kv_heads / a.kv_split, kv / a.kv_split, L, t1 - 1, tile0 + w,
-                           tile0 + n_tiles, kWaves, a.scale_log2, lane);
+                           tile0 + n_tiles, W, a.scale_log2, lane);
   }
 
-  // ---- merge the four waves ----
+  // ---- merge the W waves ----
   float (*sm_m)[R] = reinterpret_cast<float (*)[R]>(lds);
-  float (*sm_l)[R] = reinterpret_cast<float (*)[R]>(lds + kWaves * R);
-  float (*sm_o)[R][D + 4] = reinterpret_cast<float (*)[R][D + 4]>(lds + 2 * kWaves * R);
+  float (*sm_l)[R] = reinterpret_cast<float (*)[R]>(lds + W * R);
+  float (*sm_o)[R][D + 4] = reinterpret_cast<float (*)[R][D + 4]>(lds + 2 * W * R);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lr = row_sum4(st.l[nt]);
@@ -305,11 +306,11 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
     const int r = nt * 16 + n;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][r]);
+    for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v][r]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ls = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
+    for (int v = 0; v < W; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
     const float f = (Ls > 0.f) ? fast_exp2(st.m[nt] - Mu) / Ls : 0.f;
     if (r < G) {
 #pragma unroll
@@ -329,11 +330,11 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   const int slot = uo ? uo->slot + p : p;
   // four channels per thread: 16-byte LDS reads (rows of D + 4 floats stay
   // 16-byte aligned), 16-byte fp32 or 8-byte bf16 stores
-  for (int i = threadIdx.x; i < G * D / 4; i += kThreads) {
+  for (int i = threadIdx.x; i < G * D / 4; i += kT) {
     const int r = 4 * i / D, d = 4 * i % D;
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sm_o[0][r][d]);
 #pragma unroll
-    for (int u = 1; u < kWaves; ++u) v += *reinterpret_cast<const f32x4_t*>(&sm_o[u][r][d]);
+    for (int u = 1; u < W; ++u) v += *reinterpret_cast<const f32x4_t*>(&sm_o[u][r][d]);
     if (!partial)
       store4(out + ((size_t)row * a.num_heads + kv * G + r) * D + d, v);
     else
@@ -342,10 +343,10 @@ __device__ __forceinline__ void decode_partition_at(const DecodeArgs& a, int p, 
   if (partial && threadIdx.x < G) {
     const int r = threadIdx.x;
     float M = -INFINITY;
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][r]);
+    for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v][r]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ls = 0.f;
-    for (int v = 0; v < kWaves; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
+    for (int v = 0; v < W; ++v) Ls += sm_l[v][r] * fast_exp2(sm_m[v][r] - Mu);
     part_lse[(head0 + r) * stride + slot] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
   }
 }
@@ -408,7 +409,7 @@ __device__ __forceinline__ void decode_wave_partition(const DecodeArgs& a, int p
 
 // As decode_partition_at, reading the query row (sequence b's only new token
 // when query_start_loc is given, else row b) and seq_lens[b] itself.
-template <class Tile, int D, int NT, class OutT>
+template <class Tile, int D, int NT, class OutT, int W = kWaves>
 __device__ __forceinline__ void decode_partition(const DecodeArgs& a, int p, int kv, int b, float* lds) {
   int row = b;
   if (a.query_start_loc) {
@@ -416,7 +417,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, int p, int
     if (q1 - q0 != 1 || q1 > a.num_tokens || q0 < 0) return;
     row = q0;
   }
-  decode_partition_at<Tile, D, NT, OutT>(a, p, kv, b, row, a.seq_lens[b], lds);
+  decode_partition_at<Tile, D, NT, OutT, W>(a, p, kv, b, row, a.seq_lens[b], lds);
 }
 
 }  // namespace

@@ -41,6 +41,10 @@ struct DecodeArgs {
   // num_kv_heads and the kv index then count those units, and the cache's kv
   // head is kv / kv_split of num_kv_heads / kv_split.
   int kv_split = 1;
+  // waves per work-group of the one-work-group-per-partition decode (G <= 16):
+  // 4, or 8 when the grid holds at most one work-group per compute unit, so
+  // that each wave walks half as many tiles one after another
+  int waves = 4;
 };
 
 // Balanced ("stream") decode: persistent waves, each owning an equal slice of

@@ -135,19 +135,43 @@ def test_decode_edge_shapes(dtype, d, hq, hkv):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_g32_round_robin_schedule(d):
-    """bf16 with G = 32 (two row blocks per wave): the four waves of a work-group
-    take a partition's 32-token tiles round-robin through the alternating
-    double-buffered schedule (stride 4, clamped prefetches past the last
-    tile).  Every length from 1 to 300 tokens, so each wave's first and last
-    tile positions, and partitions with fewer tiles than waves, all occur;
-    unsplit and in 64- and 160-token partitions."""
-    lens = np.arange(1, 301)
+    """bf16 with G = 32 over a page pool above 512 MiB (the library then keeps
+    each kv head's 32 query heads in one unit: two row blocks per wave): the
+    waves of a work-group take a partition's 32-token tiles round-robin through
+    the alternating double-buffered schedule (stride 4, clamped prefetches past
+    the last tile).  Every length from 1 to 300 tokens, so each wave's first and
+    last tile positions, and partitions with fewer tiles than waves, all occur,
+    plus one 8192-token sequence; unsplit and in 64- and 160-token partitions."""
+    lens = np.concatenate([np.arange(1, 301), [8192]])
+    pool_tokens = 1 << 20                    # K + V of 2^20 tokens: 512 MiB at d = 128, 256 MiB at d = 64
+    slack = (pool_tokens * (128 // d) // 16 + 16) / float(sum((L + 15) // 16 for L in lens))
     bt = wl.make_batch(name="g32", seed=d + 32, num_heads=32, num_kv_heads=1, head_dim=d, block_size=16,
-                       seq_lens=lens, query_lens=np.ones(len(lens), np.int64), dtype=wl.BF16, poison_slack=True)
+                       seq_lens=lens, query_lens=np.ones(len(lens), np.int64), dtype=wl.BF16, poison_slack=True,
+                       slack_frac=slack)
+    assert bt.num_blocks * 16 * 2 * d * 2 > (512 << 20)
     poison_tails(bt)
     dev = DeviceBatch(bt)
     ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, 1, bt.scale)
     for partition in (0, 64, 160):
+        assert_parity(host(dev.decode(partition)), ref, wl.BF16, f"{bt.describe()} P={partition}")
+
+
+@pytest.mark.parametrize("num_seqs", [37, 300])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_g32_split_units(d, num_seqs):
+    """bf16 with G = 32 over a pool the last-level cache holds: each kv head's
+    query heads run as two units of 16 rows whose work-groups are paired onto
+    one XCD (a grid that is not a multiple of 16 work-groups takes the
+    remainder pairing too).  37 sequences: one work-group per compute unit or
+    fewer, 8 waves each; 300 sequences: 4 waves.  Unsplit and in 64-token
+    partitions."""
+    lens = np.arange(1, 301)[:: 300 // num_seqs][:num_seqs] if num_seqs < 300 else np.arange(1, 301)
+    bt = wl.make_batch(name="g32s", seed=d + num_seqs, num_heads=32, num_kv_heads=1, head_dim=d, block_size=16,
+                       seq_lens=lens, query_lens=np.ones(len(lens), np.int64), dtype=wl.BF16, poison_slack=True)
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    ref = decode_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens, 1, bt.scale)
+    for partition in (0, 64):
         assert_parity(host(dev.decode(partition)), ref, wl.BF16, f"{bt.describe()} P={partition}")
 
 
