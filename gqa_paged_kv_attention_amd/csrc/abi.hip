@@ -515,11 +515,18 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
                     max_seq_len, dims, scale, partition_size, workspace, workspace_bytes, s);
 }
 
-// Shared-prefix decode (bf16).  Each role is cut to give about
-// kSharedUnits work-groups (two per CU): prefix chunks of 512..2048 keys
-// (whole 64-key tiles) over num_groups x row tiles x Hkv; suffix partitions of
-// partition_size tokens, or, when the library picks, of at least 256 tokens
-// over num_seqs x Hkv.  max_seq_len bounds both the prefixes and the suffixes.
+// Shared-prefix decode (bf16).  Prefix chunks of 512..2048 keys (whole 64-key
+// tiles) over num_groups x row tiles x Hkv, cut to give about three prefix
+// work-groups per four compute units: the matrix-bound prefix units then hold
+// under half of the resident work-group slots, and the HBM-bound suffix
+// decodes run beside them from the start (4 groups x 64 sequences, 4096-token
+// prefix: 108.8 us with about two prefix work-groups per compute unit, which
+// filled every slot before any suffix started; 89.4 us at three per four;
+// 89.2 us at one per two, which slowed the 4 x 16, 2048-token batch from 27.2
+// to 29.6 us).  Suffix partitions of partition_size tokens or, when the
+// library picks, of at least 256 tokens, cut to give about kSharedUnits
+// work-groups over num_seqs x Hkv.  max_seq_len bounds both the prefixes and
+// the suffixes.
 constexpr long long kSharedUnits = 512;
 
 struct SharedPrefixPlan {
@@ -539,7 +546,8 @@ bool shared_prefix_plan(const gqa_dims& d, int32_t num_groups, int32_t max_group
   pl->row_tiles = (int)(((long long)max_group_size * G + gqa::prefill_lds_rows_per_group() - 1) /
                         gqa::prefill_lds_rows_per_group());
   const long long chunk_units = std::max(1LL, (long long)num_groups * pl->row_tiles * d.num_kv_heads);
-  const long long chunks_goal = std::max(1LL, (kSharedUnits + chunk_units - 1) / chunk_units);
+  const long long prefix_goal = std::max(1LL, (long long)device_cus() * 3 / 4);
+  const long long chunks_goal = std::max(1LL, (prefix_goal + chunk_units - 1) / chunk_units);
   pl->chunk_tokens = std::min(2048, std::max(512, round_up((len + chunks_goal - 1) / chunks_goal, 64)));
   pl->prefix_chunks = (int)((len + pl->chunk_tokens - 1) / pl->chunk_tokens);
   if (partition_size > 0) {
