@@ -43,7 +43,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # `bench.py --copy-calibration`.  Valid only for the decode sources it was
 # measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "d83f81b32b940fa87e6dced706389c467a5ccc6121324a1138f08539f62c7943", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669467847, "write_bytes_per_call": 8542080, "hbm_bytes_per_call": 678009927, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "bf5edaefd6ce02aa7f5797f92708b206f3d0173143cbdcbe858507a33084f239", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669617077, "write_bytes_per_call": 8541984, "hbm_bytes_per_call": 678159061, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
