@@ -86,33 +86,44 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteArgs a)
   for (int e = 0; e < VEC; ++e) vdst[(size_t)e * BS] = vals[e];
 }
 
-// Batches with prefill chunks: one work-group (D threads, thread d = channel
-// d) per (16-position group, kv head).  A sequence's new positions
+// Batches with prefill chunks: one work-group per 16-position group of a
+// sequence's new positions, for every kv head.  A sequence's new positions
 // [seq_len - q_len, seq_len) are cut at multiples of 16; each group lies in one
-// page (pages hold 16, 32 or 64 tokens) and its value elements for channel d
-// are one 32-byte (bf16) or 64-byte (fp32) run of the channel-major page, so
-// thread d writes that run whole: the run is read first when the group is
-// partial (the other slots keep what they hold).  Writing one element per
-// store instead leaves partial sectors, which memory completes with a read
-// (0.6 TB/s on a batch of 8k new tokens).  Key rows are token-major: thread d
-// writes element d of each new token's row (one contiguous store per token).
-// Precondition (as in any paged allocator): a page receiving one sequence's
-// new tokens receives no other sequence's.  The work-group finds its
-// sequence by a scan of the per-sequence group counts, D sequences at a time.
+// page (pages hold 16, 32 or 64 tokens).  Key rows are token-major: the group's
+// rows are copied as 16-byte chunks.  In the channel-major value page the
+// group's values of channel d are one 32-byte (bf16) or 64-byte (fp32) run, so
+// the work-group stages the group's value rows in LDS and writes each run whole
+// from there, the lanes of one run side by side in one store instruction; the
+// run is read first when the group is partial (the other slots keep what they
+// hold).  Writing one element per store instead leaves partial sectors, which
+// memory completes with a read (0.6 TB/s on a batch of 8k new tokens).  Kv
+// heads go through LDS kCwPassBytes at a time.  Precondition (as in any paged
+// allocator): a page receiving one sequence's new tokens receives no other
+// sequence's.  The work-group finds its sequence by a scan of the per-sequence
+// group counts, kThreads sequences at a time.
 constexpr int kGroup = 16;
 constexpr int kGroupMaxSeqs = 1024;
+constexpr int kCwPassBytes = 32768;      // value rows staged per pass (before padding)
 
 template <int D, int BS, class T>
-__global__ __launch_bounds__(D) void cache_write_group_kernel(CacheWriteArgs a) {
-  __shared__ int s_tot[D / 64];
+__global__ __launch_bounds__(kThreads) void cache_write_group_kernel(CacheWriteArgs a) {
+  constexpr int E = 16 / (int)sizeof(T);              // elements per 16-byte chunk
+  constexpr int CPR = D / E;                          // chunks per row (one token, one kv head)
+  constexpr int RUN = kGroup / E;                     // chunks per value run
+  constexpr int KVP = kCwPassBytes / (kGroup * D * (int)sizeof(T));   // kv heads per pass
+  constexpr int ROW = D + E;                          // LDS row stride (elements): runs of two rows 8 apart
+                                                      // fall on different banks
+  static_assert(KVP >= 1 && RUN >= 1, "pass and run sizes");
+  __shared__ __attribute__((aligned(16))) T s_v[KVP * kGroup * ROW];
+  __shared__ int s_tot[kThreads / 64];
   __shared__ int s_found[5];                 // sequence, group index, q0, first new position, seq_len
-  const int g = blockIdx.x, kv = blockIdx.y, d = threadIdx.x;
+  const int g = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_found[0] = -1;
   __syncthreads();
   int base = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += D) {
-    const int b = c0 + d;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += kThreads) {
+    const int b = c0 + threadIdx.x;
     int cnt = 0, q0 = 0, p0 = 0, L = 0;
     if (b < a.num_seqs) {
       q0 = a.query_start_loc[b];
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(D) void cache_write_group_kernel(CacheWriteArgs a) 
     __syncthreads();
     int incl = base + x, total = 0;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
+    for (int i = 0; i < kThreads / 64; ++i) {
       incl += i < w ? s_tot[i] : 0;
       total += s_tot[i];
     }
@@ -155,30 +166,41 @@ __global__ __launch_bounds__(D) void cache_write_group_kernel(CacheWriteArgs a) 
   if (lo >= hi) return;
   const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + P / BS];
   if ((unsigned)page >= (unsigned)a.num_blocks) return;
-  const size_t pbase = ((size_t)page * a.num_kv_heads + kv) * (size_t)(BS * D);
+  const int Hkv = a.num_kv_heads;
   const int slot0 = P % BS;
+  const bool partial = lo > P || hi < P + kGroup;
   const T* key = reinterpret_cast<const T*>(a.key);
   const T* value = reinterpret_cast<const T*>(a.value);
-  T* kcache = reinterpret_cast<T*>(a.key_cache) + pbase;
-  T* vrun = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)d * BS + slot0;
-  constexpr int RV = kGroup * sizeof(T) / 16;          // 16-byte pieces of a value run
-  T vals[kGroup];
-  if (lo > P || hi < P + kGroup) {
-#pragma unroll
-    for (int r = 0; r < RV; ++r) *reinterpret_cast<uint4*>(vals + r * 16 / sizeof(T)) = ld16(vrun + r * 16 / sizeof(T));
-  }
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    const int pos = P + j;
-    if (pos >= lo && pos < hi) {
-      const size_t src = ((size_t)(q0 + pos - p0) * a.num_kv_heads + kv) * D + d;
-      vals[j] = value[src];
-      kcache[(size_t)(slot0 + j) * D + d] = key[src];
+  for (int kv0 = 0; kv0 < Hkv; kv0 += KVP) {
+    const int nkv = min(KVP, Hkv - kv0);
+    // key rows to their page rows, value rows to LDS: chunk i = (kv, row j, chunk c)
+    for (int i = threadIdx.x; i < nkv * kGroup * CPR; i += kThreads) {
+      const int c = i % CPR, j = (i / CPR) % kGroup, kvl = i / (CPR * kGroup);
+      const int pos = P + j;
+      if (pos < lo || pos >= hi) continue;
+      const size_t src = ((size_t)(q0 + pos - p0) * Hkv + kv0 + kvl) * D + c * E;
+      const uint4 kx = ld16(key + src), vx = ld16(value + src);
+      const size_t pbase = ((size_t)page * Hkv + kv0 + kvl) * (size_t)(BS * D);
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.key_cache) + pbase + (size_t)(slot0 + j) * D + c * E) = kx;
+      *reinterpret_cast<uint4*>(s_v + (kvl * kGroup + j) * ROW + c * E) = vx;
     }
-  }
+    __syncthreads();
+    // value runs: output chunk i = (kv, channel d, chunk q of the run), q fastest
+    for (int i = threadIdx.x; i < nkv * D * RUN; i += kThreads) {
+      const int qq = i % RUN, d = (i / RUN) % D, kvl = i / (RUN * D);
+      const size_t pbase = ((size_t)page * Hkv + kv0 + kvl) * (size_t)(BS * D);
+      T* dst = reinterpret_cast<T*>(a.value_cache) + pbase + (size_t)d * BS + slot0 + qq * E;
+      T vals[E];
+      if (partial) *reinterpret_cast<uint4*>(vals) = ld16(dst);
 #pragma unroll
-  for (int r = 0; r < RV; ++r)
-    *reinterpret_cast<uint4*>(vrun + r * 16 / sizeof(T)) = *reinterpret_cast<const uint4*>(vals + r * 16 / sizeof(T));
+      for (int e = 0; e < E; ++e) {
+        const int j = qq * E + e, pos = P + j;
+        if (pos >= lo && pos < hi) vals[e] = s_v[(kvl * kGroup + j) * ROW + d];
+      }
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+    }
+    __syncthreads();                           // s_v is refilled by the next pass
+  }
 }
 
 template <class T>
@@ -202,9 +224,9 @@ hipError_t dispatch(const CacheWriteArgs& a, int D, int block_size, hipStream_t 
   if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
   return with_block_size(block_size, [&](auto bs) {
     constexpr int BS = decltype(bs)::value;
-    const dim3 grid((unsigned)groups, a.num_kv_heads);
-    if (D == 64) return launch_kernel(cache_write_group_kernel<64, BS, T>, grid, dim3(64), 0, s, a);
-    return launch_kernel(cache_write_group_kernel<128, BS, T>, grid, dim3(128), 0, s, a);
+    const dim3 grid((unsigned)groups);
+    if (D == 64) return launch_kernel(cache_write_group_kernel<64, BS, T>, grid, dim3(kThreads), 0, s, a);
+    return launch_kernel(cache_write_group_kernel<128, BS, T>, grid, dim3(kThreads), 0, s, a);
   });
 }
 
