@@ -202,8 +202,9 @@ __device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq, int bloc
 // the grid holds at most one work-group per compute unit).  Sequence b is
 // split into n = ceil(L / partition_size) partitions of nearly equal length
 // (whole 32-token tiles); the work-group owns partition p of one (sequence, kv
-// head), its waves share the partition's tiles and merge through LDS.  With n == 1 the work-group writes `out`; otherwise it writes the
-// partition's normalised output and log-sum-exp for the split-K reduce kernel.
+// head), its waves share the partition's tiles and merge through LDS.  With
+// n == 1 the work-group writes `out`; otherwise it writes the partition's
+// normalised output and log-sum-exp for the split-K reduce kernel.
 // ---------------------------------------------------------------------------
 // Waves per SIMD the decode kernels are compiled for: two when a double-buffered
 // K/V tile (2 x 2 x 32 tokens x D x elem bytes per wave) fits next to one row
