@@ -182,7 +182,8 @@ def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
 #   mixed_decode   the mixed batch's 205 decodes alone, same call
 #   longctx512     16 x 32k tokens, paged_gqa_decode with 512-token partitions
 #   longctx        the same with the library's split
-PROFILE_LEGS = ("decode_step", "mixed", "mixed_prefill", "mixed_decode", "longctx512", "longctx")
+#   mqa            paged_gqa_decode on the Llama-2-7B sweep with one kv head (Hq = 32)
+PROFILE_LEGS = ("decode_step", "mixed", "mixed_prefill", "mixed_decode", "longctx512", "longctx", "mqa")
 
 
 def profile_leg(name, calls, dev, stream, seed):
@@ -207,7 +208,7 @@ def profile_leg(name, calls, dev, stream, seed):
                "mixed_decode": np.where(ql == 1)[0]}[name]
         f = mixed_part_call(mb, idx, mq, mkc, mvc, mt, ml, dev)
     else:
-        bt = wl.longctx_splitk(seed=5)
+        bt = wl.longctx_splitk(seed=5) if name.startswith("longctx") else wl.llama2_7b_sweep(1, seed=3)
         q, kc, vc, tb, sl = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.block_tables), up(bt.seq_lens)
         out = torch.empty(bt.num_seqs, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
         part = 512 if name == "longctx512" else 0
