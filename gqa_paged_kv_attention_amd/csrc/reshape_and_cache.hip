@@ -111,8 +111,9 @@ __global__ __launch_bounds__(kThreads) void cache_write_group_kernel(CacheWriteA
   constexpr int CPR = D / E;                          // chunks per row (one token, one kv head)
   constexpr int RUN = kGroup / E;                     // chunks per value run
   constexpr int KVP = kCwPassBytes / (kGroup * D * (int)sizeof(T));   // kv heads per pass
-  constexpr int ROW = D + E;                          // LDS row stride (elements): runs of two rows 8 apart
-                                                      // fall on different banks
+  // LDS row stride (elements): one 16-byte chunk of padding, so that the rows
+  // the lanes of one run read (8 apart) fall on different banks
+  constexpr int ROW = D + E;
   static_assert(KVP >= 1 && RUN >= 1, "pass and run sizes");
   __shared__ __attribute__((aligned(16))) T s_v[KVP * kGroup * ROW];
   __shared__ int s_tot[kThreads / 64];
