@@ -47,6 +47,14 @@ def calls():
                     lambda o, w, d=da, bt=bt, P=P: ops.paged_gqa_decode_append(
                         d.query, d.new_key, d.new_value, d.key_cache, d.value_cache, d.block_tables, d.seq_lens,
                         bt.max_seq_len, bt.scale, partition_size=P, out=o, workspace=w)))
+    # MQA over a small cache: two 16-row units per kv head on one XCD, 8 waves per work-group
+    qb = wl.llama2_7b_sweep(1, seed=15, num_seqs=37)
+    dq = DeviceBatch(qb)
+    n = ops.decode_workspace_size(dims_of(qb, dq), qb.max_seq_len, 0)
+    out.append(("decode_mqa", (qb.num_seqs, qb.num_heads, qb.head_dim), n,
+                lambda o, w, d=dq, bt=qb: ops.paged_gqa_decode(
+                    d.query, d.key_cache, d.value_cache, d.block_tables, d.seq_lens, bt.max_seq_len, bt.scale,
+                    out=o, workspace=w)))
     mb = wl.mixed_chunked(seed=13, num_seqs=40, token_budget=1500)
     dm = DeviceBatch(mb)
     n = ops.mixed_workspace_size(dims_of(mb, dm), mb.num_tokens, mb.max_seq_len, 0)
@@ -73,7 +81,7 @@ def calls():
 
 
 CALLS = None
-N_CALLS = 7
+N_CALLS = 8
 
 
 def get_calls():
