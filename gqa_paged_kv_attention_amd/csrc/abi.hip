@@ -436,7 +436,15 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     sa.num_tokens = num_tokens;
     sa.max_query_len = max_query_len;
     sa.group = G;
-    sa.rows_per_group = gqa::prefill_lds_rows_per_group();
+    // Prefill-heavy batches (on average 1024 or more query rows, tokens x G,
+    // per sequence) run 8-wave work-groups with 256-row prefill tiles: each
+    // K/V tile is staged once for twice the rows (16 x 512 new tokens on
+    // 3584-token prefixes: 7% faster; cross-attention, 16 chunks of 256 rows
+    // over 1024..6400 encoder tokens: 1-6%).  Shorter chunks lose more to the
+    // coarser row tiles than they gain (51 chunks of 624 rows each on average:
+    // 102 -> 115 us).
+    const int waves = (G <= 16 && (long long)num_tokens * G >= 1024LL * dims.num_seqs) ? 8 : 4;
+    sa.rows_per_group = gqa::prefill_lds_rows_per_group(waves);
     sa.max_blocks_per_seq = dims.max_blocks_per_seq;
     sa.block_size = dims.block_size;
     sa.partition_size = psize;
@@ -467,7 +475,8 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     d.scale_log2 = scale_log2;
     ma.units = units;
     ma.unit_count = count;
-    hipError_t e = gqa::launch_mixed(ma, dims.head_dim, dims.block_size, out_f32, (int)(cap * dims.num_kv_heads), s);
+    hipError_t e =
+        gqa::launch_mixed(ma, dims.head_dim, dims.block_size, out_f32, (int)(cap * dims.num_kv_heads), waves, s);
     if (e != hipSuccess || nparts <= 1) return status_from(e);
     gqa::ReduceArgs r;
     r.out = out;

@@ -161,8 +161,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bo
                           int grid_groups, hipStream_t stream);
 // Mixed batch, bf16: the scheduling pass writes the work units, ordered by
 // decreasing cost; the fused kernel runs unit i / Hkv for kv head i % Hkv.
-// Rows of a prefill unit (depends only on the build):
-int prefill_lds_rows_per_group();
+// Rows of a prefill unit for a launch of `waves` waves per work-group (4 or 8;
+// 32 rows per wave):
+int prefill_lds_rows_per_group(int waves = 4);
+// Decode partitions per pack record: one per wave of a 4-wave work-group (an
+// 8-wave work-group of the fused kernel runs them on its first four waves).
+constexpr int kPackSlots = 4;
 // A scheduled unit, four 16-byte slots, read by its work-group together with
 // the unit count.
 //  - Prefill row tile rt of sequence b: s[0] = {b, rt, q0, q1} (the sequence's
@@ -232,7 +236,7 @@ hipError_t launch_shared_prefix(const SharedPrefixArgs& a, int head_dim, int blo
                                 hipStream_t stream);
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream);
-hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups, int waves,
                         hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, bool out_f32, int num_seqs, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int head_dim, int block_size, bool kv_f32,

@@ -336,11 +336,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
 // and matrix-bound prefill tiles then share the device instead of running one
 // after the other.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int BS, class OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+template <int D, int NT, int BS, class OutT, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void mixed_kernel(MixedArgs a) {
-  typedef PrefillLds<D, kLdsNTW> S;
-  __shared__ __attribute__((aligned(16))) char lds[MixedLds<D, NT>::kBytes];
+  typedef PrefillLds<D, kLdsNTW, W> S;
+  __shared__ __attribute__((aligned(16))) char lds[MixedLds<D, NT, W>::kBytes];
   const int Hkv = a.prefill.num_kv_heads;
   const int slot = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
   // the record is read together with the count (slot < the list's capacity)
@@ -352,44 +352,51 @@ void mixed_kernel(MixedArgs a) {
     uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
     const int4 p0 = a.units[slot].s[2], p1 = a.units[slot].s[3];
     const int first_pages[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    prefill_unit<D, kLdsNTW, BS, OutT>(a.prefill, u.x, u.y, u.z, u.w, u1.x, kv, sK, sK + 2 * S::KBUF, 0, UnitOut(),
-                                       first_pages);
+    prefill_unit<D, kLdsNTW, BS, OutT, W>(a.prefill, u.x, u.y, u.z, u.w, u1.x, kv, sK, sK + 2 * S::KBUF, 0,
+                                          UnitOut(), first_pages);
   } else if (u1.x == kUnitWholeGroup) {
-    decode_partition_at<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - u.y, kv, u.x, u.z, u.w,
-                                                      reinterpret_cast<float*>(lds));
+    decode_partition_at<TileBF16<D, BS>, D, NT, OutT, W>(a.decode, -1 - u.y, kv, u.x, u.z, u.w,
+                                                         reinterpret_cast<float*>(lds));
   } else {
-    // one short decode partition per wave (the branch is uniform per wave)
+    // one short decode partition per wave, four to a record (the branch is
+    // uniform per wave; with 8 waves the last four have none)
     const int w = wave_id();
-    const int4 e = a.units[slot].s[w];
-    if (e.x >= 0) decode_wave_partition<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - e.y, kv, e.x, e.z, e.w);
+    if (w < kPackSlots) {
+      const int4 e = a.units[slot].s[w];
+      if (e.x >= 0) decode_wave_partition<TileBF16<D, BS>, D, NT, OutT>(a.decode, -1 - e.y, kv, e.x, e.z, e.w);
+    }
   }
 }
 
 template <int D, int BS, class OutT>
-hipError_t mixed_dispatch(const MixedArgs& a, int groups, hipStream_t s) {
-  if (a.prefill.group <= 16)
-    return launch_kernel(mixed_kernel<D, 1, BS, OutT>, dim3(groups), dim3(kThreads), 0, s, a);
-  else
-    return launch_kernel(mixed_kernel<D, 2, BS, OutT>, dim3(groups), dim3(kThreads), 0, s, a);
+hipError_t mixed_dispatch(const MixedArgs& a, int groups, int waves, hipStream_t s) {
+  if (a.prefill.group > 16)
+    return launch_kernel(mixed_kernel<D, 2, BS, OutT, kWaves>, dim3(groups), dim3(kThreads), 0, s, a);
+  if (waves == 2 * kWaves)
+    return launch_kernel(mixed_kernel<D, 1, BS, OutT, 2 * kWaves>, dim3(groups), dim3(2 * kThreads), 0, s, a);
+  return launch_kernel(mixed_kernel<D, 1, BS, OutT, kWaves>, dim3(groups), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
-int prefill_lds_rows_per_group() { return PrefillLds<128, kLdsNTW>::kRowsPerGroup; }
+int prefill_lds_rows_per_group(int waves) {
+  return waves == 2 * kWaves ? PrefillLds<128, kLdsNTW, 2 * kWaves>::kRowsPerGroup
+                             : PrefillLds<128, kLdsNTW>::kRowsPerGroup;
+}
 
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream) {
   return launch_kernel(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
 }
 
-hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups,
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups, int waves,
                         hipStream_t stream) {
   return with_block_size(block_size, [&](auto bs) {
     constexpr int BS = decltype(bs)::value;
     if (head_dim == 64)
-      return out_f32 ? mixed_dispatch<64, BS, float>(a, grid_groups, stream)
-                     : mixed_dispatch<64, BS, uint16_t>(a, grid_groups, stream);
-    return out_f32 ? mixed_dispatch<128, BS, float>(a, grid_groups, stream)
-                   : mixed_dispatch<128, BS, uint16_t>(a, grid_groups, stream);
+      return out_f32 ? mixed_dispatch<64, BS, float>(a, grid_groups, waves, stream)
+                     : mixed_dispatch<64, BS, uint16_t>(a, grid_groups, waves, stream);
+    return out_f32 ? mixed_dispatch<128, BS, float>(a, grid_groups, waves, stream)
+                   : mixed_dispatch<128, BS, uint16_t>(a, grid_groups, waves, stream);
   });
 }
 

@@ -32,10 +32,11 @@ constexpr float kLazyRescale = 8.f;      // log2 growth of a row max before O is
 constexpr int kKeyTile = 64;             // keys per iteration
 constexpr int kTileBlocks = kKeyTile / kHalf;   // 16-token blocks per tile, each inside one page
 
-template <int D, int NTW>
+template <int D, int NTW, int W = kWaves>
 struct PrefillLds {
+  static constexpr int kT = W * kWave;               // threads of the work-group
   static constexpr int kRowsPerWave = NTW * 16;
-  static constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+  static constexpr int kRowsPerGroup = W * kRowsPerWave;
   static constexpr int KC = D / 32;                 // 16-byte chunks of a row per Q.K^T product
   static constexpr int DT = D / 16;                 // 16-channel output blocks
   static constexpr int KROW = D + 16;               // LDS row stride of the key tile (elements)
@@ -43,9 +44,9 @@ struct PrefillLds {
   static constexpr int KBUF = kKeyTile * KROW;      // one key buffer (elements)
   static constexpr int VBUF = D * VROW;             // one value buffer (elements)
   static constexpr int kBytes = 2 * (KBUF + VBUF) * 2;
-  static constexpr int CH = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile, K and V each
-  // chunk i of a thread comes from 16-token block i * PI + (thread / (kThreads / PI)) of the tile
-  static constexpr int PI = kThreads / (2 * D);
+  static constexpr int CH = kKeyTile * D / 8 / kT;   // 16-byte chunks per thread per tile, K and V each
+  // chunk i of a thread comes from 16-token block i * PI + (thread / (kT / PI)) of the tile
+  static constexpr int PI = kT / (2 * D);
   static_assert(PI == 1 || PI == 2 || PI == 4, "a copy chunk spans 1, 2 or 4 blocks");
 };
 
@@ -65,17 +66,17 @@ __device__ __forceinline__ int key_row(int t) { return t ^ ((t >> 2) & 4); }
 // its element offset from the first token of its 16-token block (key rows D
 // elements apart, value channels BS apart) and in the LDS tile.  The chunk's
 // block is wave-uniform: i * PI + pw.
-template <int D, int NTW, int BS>
+template <int D, int NTW, int BS, int W = kWaves>
 struct TileCopyPlan {
-  typedef PrefillLds<D, NTW> S;
+  typedef PrefillLds<D, NTW, W> S;
   int k_src[S::CH], k_dst[S::CH];
   int v_src[S::CH], v_dst[S::CH], v_tok[S::CH];
   int pw;                                           // wave-uniform block offset of chunk 0
   __device__ __forceinline__ void init() {
-    pw = S::PI == 1 ? 0 : uniform(threadIdx.x / (kThreads / S::PI));
+    pw = S::PI == 1 ? 0 : uniform(threadIdx.x / (S::kT / S::PI));
 #pragma unroll
     for (int i = 0; i < S::CH; ++i) {
-      const int ci = threadIdx.x + i * kThreads;
+      const int ci = threadIdx.x + i * S::kT;
       const int token = ci / (D / 8), col = ci % (D / 8);        // token / 16: block of chunk i
       k_src[i] = (token % kHalf) * D + col * 8;
       k_dst[i] = key_row(token) * S::KROW + col * 8;
@@ -104,10 +105,10 @@ struct TilePtrs {
   const uint16_t* v[kTileBlocks];
 };
 
-template <int D, int NTW, int BS>
-__device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW, BS>& plan,
+template <int D, int NTW, int BS, int W = kWaves>
+__device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const TileCopyPlan<D, NTW, BS, W>& plan,
                                                const TilePtrs& tp) {
-  typedef PrefillLds<D, NTW> S;
+  typedef PrefillLds<D, NTW, W> S;
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) {
     kreg[i] = ld16(plan.block_of(i, tp.k) + plan.k_src[i]);
@@ -117,10 +118,10 @@ __device__ __forceinline__ void load_tile_regs(uint4* kreg, uint4* vreg, const T
 
 // Registers -> LDS; values are converted to fp16, and with `tail` set those of
 // tokens at or past L become 0.
-template <int D, int NTW, int BS>
+template <int D, int NTW, int BS, int W = kWaves>
 __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const uint4* kreg, const uint4* vreg,
-                                               const TileCopyPlan<D, NTW, BS>& plan, int tile_base, int L, bool tail) {
-  typedef PrefillLds<D, NTW> S;
+                                               const TileCopyPlan<D, NTW, BS, W>& plan, int tile_base, int L, bool tail) {
+  typedef PrefillLds<D, NTW, W> S;
 #pragma unroll
   for (int i = 0; i < S::CH; ++i) *reinterpret_cast<uint4*>(sK + plan.k_dst[i]) = kreg[i];
   uint32_t w[S::CH][4];
@@ -159,11 +160,11 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* sK, uint16_t* sV, const
 // each.  `first_pages`, when given (t_begin = 0 only), holds
 // block_tables[b][min(j, pages - 1)] for j = 0..7, the entries of tiles 0 and
 // 1, already loaded with the unit.
-template <int D, int NTW, int BS, class OutT>
+template <int D, int NTW, int BS, class OutT, int W = kWaves>
 __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt, int q0, int q1, int seq_len, int kv,
                                              uint16_t* sK, uint16_t* sV, int t_begin = 0,
                                              const UnitOut& uo = UnitOut(), const int* first_pages = nullptr) {
-  typedef PrefillLds<D, NTW> S;
+  typedef PrefillLds<D, NTW, W> S;
   const int G = a.group;
   const int q_len = q1 - q0;
   if (q1 > a.num_tokens || q0 < 0) return;
@@ -221,7 +222,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
   const uint32_t page_bytes = (uint32_t)a.num_kv_heads * (BS * D * 2);
   constexpr int kEntries = kKeyTile / BS;           // block-table entries per tile: 4, 2 or 1
 
-  TileCopyPlan<D, NTW, BS> plan;
+  TileCopyPlan<D, NTW, BS, W> plan;
   plan.init();
   // Raw block-table entries of tile t (clamped to the last tile and page).
   // They are loaded one iteration before they are used, with scalar loads
@@ -243,7 +244,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
       tp.k[j] = reinterpret_cast<const uint16_t*>(kc + off) + slot * D;
       tp.v[j] = reinterpret_cast<const uint16_t*>(vc + off) + slot;
     }
-    load_tile_regs<D, NTW, BS>(kr, vr, plan, tp);
+    load_tile_regs<D, NTW, BS, W>(kr, vr, plan, tp);
   };
 
   float m[NTW], mu[NTW];
@@ -274,7 +275,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
       issue(raw, kreg, vreg);
       fetch_pages(t_begin + 1, raw);
     }
-    store_tile_lds<D, NTW, BS>(sK, sV, kreg, vreg, plan, t_begin * kKeyTile, L, (t_begin + 1) * kKeyTile > L);
+    store_tile_lds<D, NTW, BS, W>(sK, sV, kreg, vreg, plan, t_begin * kKeyTile, L, (t_begin + 1) * kKeyTile > L);
     if (n_tiles > t_begin + 1) issue(raw, kreg, vreg);
     fetch_pages(t_begin + 2, raw);
     __syncthreads();
@@ -382,8 +383,8 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
     // a unit start while the second is still arriving.
     if (tb <= lim_hi) compute(sK + buf * S::KBUF, sV + buf * S::VBUF, tb, tb + kKeyTile - 1 > lim_lo);
     if (it + 1 < n_tiles)
-      store_tile_lds<D, NTW, BS>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan, tb + kKeyTile, L,
-                             tb + 2 * kKeyTile > L);
+      store_tile_lds<D, NTW, BS, W>(sK + (buf ^ 1) * S::KBUF, sV + (buf ^ 1) * S::VBUF, kreg, vreg, plan,
+                                    tb + kKeyTile, L, tb + 2 * kKeyTile > L);
     if (it + 2 < n_tiles) issue(raw, kreg, vreg);
     fetch_pages(it + 3, raw);
     __syncthreads();
@@ -415,11 +416,11 @@ __device__ __forceinline__ void prefill_unit(const PrefillArgs& a, int b, int rt
 constexpr int kLdsNTW = 2;
 
 // LDS of a work-group that runs either a prefill unit or a decode partition.
-template <int D, int NT>
+template <int D, int NT, int W = kWaves>
 struct MixedLds {
-  typedef PrefillLds<D, kLdsNTW> S;
+  typedef PrefillLds<D, kLdsNTW, W> S;
   static constexpr int kPrefillBytes = S::kBytes;
-  static constexpr int kDecodeBytes = DecodeMergeLds<D, NT>::kFloats * 4;
+  static constexpr int kDecodeBytes = DecodeMergeLds<D, NT, W>::kFloats * 4;
   static constexpr int kBytes = kPrefillBytes > kDecodeBytes ? kPrefillBytes : kDecodeBytes;
 };
 

@@ -468,6 +468,47 @@ def test_mixed_small_values(v_scale):
     assert_parity(out, oracle_after_write(bt, mixed=True), bt.dtype, f"{bt.describe()} V x {v_scale:g}")
 
 
+def _prefill_heavy(hq, hkv, d, bs, seed):
+    """Prefill chunks with ragged 256-row tiles beside decodes of every kind:
+    packed short ones (up to 2048 keys), whole-work-group ones (2049 and more
+    keys), a one-key decode and an empty query.  Query rows x G average 1024
+    or more per sequence, so the fused kernel runs 8-wave work-groups."""
+    G = hq // hkv
+    chunk = {1: 3700, 4: 1000, 8: 500, 16: 250}[G]
+    q_lens = [chunk, 1, 1, 1, chunk + 37, 0, 1, chunk // 2 + 3, 1]
+    prior = [0, 3000, 700, 2047, 100, 5, 2048, 1500, 0]
+    bt = wl.make_batch(name="heavy", seed=seed, num_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                       seq_lens=[a + b for a, b in zip(q_lens, prior)], query_lens=q_lens, dtype=wl.BF16,
+                       poison_slack=True)
+    assert bt.num_tokens * G >= 1024 * bt.num_seqs
+    poison_tails(bt)
+    return bt
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("d", [64, 128])
+def test_mixed_prefill_heavy_eight_waves(d, bs):
+    bt = _prefill_heavy(32, 8, d, bs, seed=d + bs)
+    dev = DeviceBatch(bt)
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale)
+    for partition in (0, 512):
+        assert_parity(host(dev.mixed(partition)), ref, bt.dtype, f"{bt.describe()} P={partition}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2), (16, 1)])
+def test_mixed_prefill_heavy_eight_waves_groups(hq, hkv):
+    bt = _prefill_heavy(hq, hkv, 128, 16, seed=hq + hkv)
+    dev = DeviceBatch(bt)
+    dev.cache_write()
+    ref = oracle_after_write(bt, mixed=True)
+    o32 = dev.mixed(0, out_dtype=torch.float32)
+    o16 = dev.mixed(0, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert_parity(host(o32), ref, bt.dtype, bt.describe())
+
+
 # --------------------------------------------------------------------------
 # full-size workloads: the whole output against the oracle, in the launch
 # configurations the benchmark times
