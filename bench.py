@@ -43,7 +43,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # `bench.py --copy-calibration`.  Valid only for the decode sources it was
 # measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "8c12b426643f277c0e043d0f9b2c9cb3be7323b0673b8824f725ef19af4565c1", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669604406, "write_bytes_per_call": 8541856, "hbm_bytes_per_call": 678146262, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "e253c6e5c26d0e3b792f59a39a74415225f323af79677383162ea0822cf90e52", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669629749, "write_bytes_per_call": 8541664, "hbm_bytes_per_call": 678171413, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
