@@ -440,10 +440,18 @@ int run_mixed(void* out, const void* query, const void* key_cache, const void* v
     // per sequence) run 8-wave work-groups with 256-row prefill tiles: each
     // K/V tile is staged once for twice the rows (16 x 512 new tokens on
     // 3584-token prefixes: 7% faster; cross-attention, 16 chunks of 256 rows
-    // over 1024..6400 encoder tokens: 1-6%).  Shorter chunks lose more to the
-    // coarser row tiles than they gain (51 chunks of 624 rows each on average:
-    // 102 -> 115 us).
-    const int waves = (G <= 16 && (long long)num_tokens * G >= 1024LL * dims.num_seqs) ? 8 : 4;
+    // over 1024..6400 encoder tokens: 1-6%; 2 to 8 chunks of 256..1024 tokens:
+    // 5-9%).  Shorter chunks lose more to the coarser row tiles than they gain
+    // (51 chunks of 624 rows each on average: 102 -> 115 us), and so do a
+    // single sequence (one 2048-token chunk: 4%; the 8-wave tiles of one chunk
+    // differ in cost along the diagonal, and one tile per compute unit leaves
+    // nothing to even them out) and a batch of fewer 4-wave tiles than compute
+    // units (one 300-token chunk: 12%).
+    const long long qrows = (long long)num_tokens * G;
+    const int waves = (G <= 16 && dims.num_seqs >= 2 && qrows >= 1024LL * dims.num_seqs &&
+                       qrows / gqa::prefill_lds_rows_per_group(4) * dims.num_kv_heads >= device_cus())
+                          ? 8
+                          : 4;
     sa.rows_per_group = gqa::prefill_lds_rows_per_group(waves);
     sa.max_blocks_per_seq = dims.max_blocks_per_seq;
     sa.block_size = dims.block_size;

@@ -471,8 +471,10 @@ def test_mixed_small_values(v_scale):
 def _prefill_heavy(hq, hkv, d, bs, seed):
     """Prefill chunks with ragged 256-row tiles beside decodes of every kind:
     packed short ones (up to 2048 keys), whole-work-group ones (2049 and more
-    keys), a one-key decode and an empty query.  Query rows x G average 1024
-    or more per sequence, so the fused kernel runs 8-wave work-groups."""
+    keys), a one-key decode and an empty query.  Query rows (tokens x G)
+    average 1024 or more per sequence over several sequences, and their
+    128-row tiles times Hkv outnumber the compute units, so the fused kernel
+    runs 8-wave work-groups."""
     G = hq // hkv
     chunk = {1: 3700, 4: 1000, 8: 500, 16: 250}[G]
     q_lens = [chunk, 1, 1, 1, chunk + 37, 0, 1, chunk // 2 + 3, 1]
@@ -480,7 +482,9 @@ def _prefill_heavy(hq, hkv, d, bs, seed):
     bt = wl.make_batch(name="heavy", seed=seed, num_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
                        seq_lens=[a + b for a, b in zip(q_lens, prior)], query_lens=q_lens, dtype=wl.BF16,
                        poison_slack=True)
-    assert bt.num_tokens * G >= 1024 * bt.num_seqs
+    rows = bt.num_tokens * G
+    assert rows >= 1024 * bt.num_seqs
+    assert rows // 128 * hkv >= torch.cuda.get_device_properties(0).multi_processor_count
     poison_tails(bt)
     return bt
 
@@ -496,7 +500,7 @@ def test_mixed_prefill_heavy_eight_waves(d, bs):
         assert_parity(host(dev.mixed(partition)), ref, bt.dtype, f"{bt.describe()} P={partition}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2), (16, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (32, 4), (64, 4)])
 def test_mixed_prefill_heavy_eight_waves_groups(hq, hkv):
     bt = _prefill_heavy(hq, hkv, 128, 16, seed=hq + hkv)
     dev = DeviceBatch(bt)
