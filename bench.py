@@ -43,7 +43,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # `bench.py --copy-calibration`.  Valid only for the decode sources it was
 # measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "e253c6e5c26d0e3b792f59a39a74415225f323af79677383162ea0822cf90e52", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669629749, "write_bytes_per_call": 8541664, "hbm_bytes_per_call": 678171413, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "db31d98f43eb069af11d7b204c04ab4f56fb7885e3980a0a02eb83e3dd26dfab", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669638452, "write_bytes_per_call": 8541824, "hbm_bytes_per_call": 678180276, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
@@ -183,7 +183,7 @@ def mixed_part_ms(mb, idx, mq, mkc, mvc, mt, ml, dev, stream, reps=50):
 #   longctx512     16 x 32k tokens, paged_gqa_decode with 512-token partitions
 #   longctx        the same with the library's split
 #   mqa            paged_gqa_decode on the Llama-2-7B sweep with one kv head (Hq = 32)
-PROFILE_LEGS = ("decode_step", "mixed", "mixed_prefill", "mixed_decode", "longctx512", "longctx", "mqa")
+PROFILE_LEGS = ("decode_step", "mixed", "mixed_prefill", "mixed_decode", "longctx512", "longctx", "mqa", "cross_chunk")
 
 
 def profile_leg(name, calls, dev, stream, seed):
@@ -207,6 +207,14 @@ def profile_leg(name, calls, dev, stream, seed):
         idx = {"mixed": np.arange(mb.num_seqs), "mixed_prefill": np.where(ql > 1)[0],
                "mixed_decode": np.where(ql == 1)[0]}[name]
         f = mixed_part_call(mb, idx, mq, mkc, mvc, mt, ml, dev)
+    elif name == "cross_chunk":
+        # 16 chunks of 256 decoder rows over the static encoder cache (8-wave launch)
+        bt = wl.cross_attention(seed=6, query_len=256)
+        q, kc, vc = up(bt.query), up(bt.key_cache), up(bt.value_cache)
+        tb, el, qsl = up(bt.block_tables), up(bt.seq_lens), up(bt.query_start_loc)
+        out = torch.empty(bt.num_tokens, bt.num_heads, bt.head_dim, dtype=torch.float32, device=dev)
+        f = lambda: ops.paged_cross_attention(q, kc, vc, tb, el, qsl, bt.max_query_len, bt.max_seq_len, bt.scale,
+                                              out=out)
     else:
         bt = wl.longctx_splitk(seed=5) if name.startswith("longctx") else wl.llama2_7b_sweep(1, seed=3)
         q, kc, vc, tb, sl = up(bt.query), up(bt.key_cache), up(bt.value_cache), up(bt.block_tables), up(bt.seq_lens)
