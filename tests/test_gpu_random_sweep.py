@@ -100,6 +100,47 @@ def test_random_mixed_and_cross(seed, causal):
     assert_parity(got, ref, bt.dtype, f"{bt.describe()} causal={causal} P={partition}")
 
 
+HEAVY_HEADS = [(hq, hkv) for hq, hkv in HEADS if 2 <= hq // hkv <= 16]
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("causal", [True, False])
+def test_random_prefill_heavy(seed, causal):
+    """Random batches that take the fused kernel's 8-wave launch (two or more
+    sequences, query rows x G averaging 1024 or more per sequence, more 128-row
+    tiles x Hkv than compute units): random heads, head size, page size and
+    lengths, with decodes among the chunks."""
+    rng, shape = draw(500 + seed)
+    hq, hkv = HEAVY_HEADS[rng.integers(len(HEAVY_HEADS))]
+    shape.update(num_heads=hq, num_kv_heads=hkv, dtype=wl.BF16)
+    G = hq // hkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = int(rng.integers(2, 9))
+    n_dec = int(rng.integers(0, B // 2 + 1))
+    rows_needed = max(1024 * B, 128 * -(-cus // hkv))
+    tokens = -(-rows_needed // G) - n_dec
+    n_chunk = B - n_dec
+    cuts = np.sort(rng.integers(0, tokens + 1, size=n_chunk - 1))
+    q_chunks = np.diff(np.concatenate([[0], cuts, [tokens]]))
+    q = np.concatenate([q_chunks, np.ones(n_dec, dtype=np.int64)])
+    rng.shuffle(q)
+    if causal:
+        L = q + rng.integers(0, 1500, size=B)
+    else:
+        L = rng.integers(1, 3000, size=B)
+    bt = wl.make_batch(name="rnd_heavy", seed=seed, seq_lens=L, query_lens=q, poison_slack=True, cross=not causal,
+                       **shape)
+    rows = bt.num_tokens * G
+    assert B >= 2 and rows >= 1024 * B and rows // 128 * hkv >= cus
+    poison_tails(bt)
+    dev = DeviceBatch(bt)
+    partition = int(rng.choice([0, 512]))
+    got = host(dev.mixed(partition) if causal else dev.cross(partition))
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale, causal=causal)
+    assert_parity(got, ref, bt.dtype, f"{bt.describe()} causal={causal} P={partition}")
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_shared_prefix(seed):
     rng, shape = draw(200 + seed)
