@@ -62,6 +62,15 @@ def calls():
                 lambda o, w, d=dm, bt=mb: ops.chunked_prefill_paged_decode(
                     d.query, d.key_cache, d.value_cache, d.block_tables, d.seq_lens, d.query_start_loc,
                     bt.max_query_len, bt.max_seq_len, bt.scale, out=o, workspace=w)))
+    # prefill-heavy: four 512-token chunks beside two decodes take the 8-wave launch
+    hb = wl.make_batch(name="heavy", seed=16, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       seq_lens=[768, 768, 768, 768, 3000, 100], query_lens=[512, 512, 512, 512, 1, 1], dtype=wl.BF16)
+    dh = DeviceBatch(hb)
+    n = ops.mixed_workspace_size(dims_of(hb, dh), hb.num_tokens, hb.max_seq_len, 0)
+    out.append(("mixed_8_waves", (hb.num_tokens, hb.num_heads, hb.head_dim), n,
+                lambda o, w, d=dh, bt=hb: ops.chunked_prefill_paged_decode(
+                    d.query, d.key_cache, d.value_cache, d.block_tables, d.seq_lens, d.query_start_loc,
+                    bt.max_query_len, bt.max_seq_len, bt.scale, out=o, workspace=w)))
     cb = wl.cross_attention(seed=14, num_seqs=6, enc_lo=100, enc_hi=2000, query_len=40)
     dc = DeviceBatch(cb)
     n = ops.cross_workspace_size(dims_of(cb, dc), cb.num_tokens, cb.max_seq_len, 0)
@@ -81,7 +90,7 @@ def calls():
 
 
 CALLS = None
-N_CALLS = 8
+N_CALLS = 9
 
 
 def get_calls():
