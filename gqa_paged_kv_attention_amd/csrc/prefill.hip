@@ -36,7 +36,7 @@ namespace {
 // groups of one kv head share an XCD and its L2).  Cost,
 // in tile steps of a work-group: a prefill row tile takes one step per 32-key
 // tile up to its last row's causal limit; a decode partition's tiles are
-// shared by the 4 waves.  One work-group of 1024 threads counts the units per
+// shared by the waves.  One work-group of 1024 threads counts the units per
 // cost bucket and list in LDS, scans, and reserves a range per sequence (the
 // order of sequences within a bucket is arbitrary; each unit's result does not
 // depend on it).

@@ -6,8 +6,9 @@
 // query head g of the group), r = j * G + g, so the G heads that share a kv
 // head share every K/V tile that is loaded ("[Performance] Use optimized
 // kernels for MQA/GQA", opening post: GQA should cut KV reads and let the dot
-// products run on matrix cores).  A work-group owns 4 waves x NTW blocks of 16
-// rows; the four waves load each 64-key tile once, cooperatively, into LDS
+// products run on matrix cores).  A work-group owns W waves (4, or 8 in the
+// launch for prefill-heavy batches) x NTW blocks of 16 rows; the waves load
+// each 64-key tile once, cooperatively, into LDS
 // (double-buffered, the next tile's global loads in flight while the current
 // one is consumed) and each wave multiplies it against its own rows:
 //   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 out),
