@@ -550,6 +550,25 @@ def test_full_mixed(partition):
         assert np.max(np.abs(host(o16) - ref)) <= 1e-2
 
 
+def test_full_uniform_prefill_eight_waves():
+    """The 8-wave launch at full size: 16 chunks of 512 new tokens on
+    3584-token prefixes (Hq = 32, Hkv = 8, d = 128, bf16).  The oracle computes
+    the first and the last sequence whole (every row of their 256-row tiles,
+    causal limits up to 4096 keys); the other sequences' outputs must be finite
+    and, as the same computation on other data, are covered by the random
+    prefill-heavy draws."""
+    bt = wl.make_batch(name="uniform", seed=11, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       seq_lens=[4096] * 16, query_lens=[512] * 16, dtype=wl.BF16)
+    assert bt.num_tokens * 4 // 128 * 8 >= torch.cuda.get_device_properties(0).multi_processor_count
+    got = host(DeviceBatch(bt).mixed(0))
+    assert np.all(np.isfinite(got))
+    seqs = [0, bt.num_seqs - 1]
+    ref = paged_attention_ref(bt.query, bt.key_cache, bt.value_cache, bt.block_tables, bt.seq_lens,
+                              bt.query_start_loc, bt.num_kv_heads, bt.scale, seqs=seqs)
+    rows = np.concatenate([np.arange(bt.query_start_loc[b], bt.query_start_loc[b + 1]) for b in seqs])
+    assert_parity(got[rows], ref[rows], bt.dtype, bt.describe() + " sequences 0 and 15")
+
+
 @pytest.mark.parametrize("name", ["mixed", "decode"])
 def test_full_cache_write_bit_exact(name):
     """reshape_and_cache at the benchmark's sizes (the mixed batch's 8166 new
