@@ -390,6 +390,9 @@ hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t stream) {
 
 hipError_t launch_mixed(const MixedArgs& a, int head_dim, int block_size, bool out_f32, int grid_groups, int waves,
                         hipStream_t stream) {
+  // the scheduling pass cut the prefill rows for this wave count: only the
+  // launches that exist for it (8 waves: G <= 16)
+  if (waves != kWaves && (waves != 2 * kWaves || a.prefill.group > 16)) return hipErrorInvalidValue;
   return with_block_size(block_size, [&](auto bs) {
     constexpr int BS = decltype(bs)::value;
     if (head_dim == 64)
