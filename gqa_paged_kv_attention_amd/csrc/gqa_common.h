@@ -208,8 +208,13 @@ struct TileBF16 {
   // Value loads stream only when one 128-byte line of a channel does not hold
   // both tiles of a pair (64-token pages): the second tile's half of the line
   // must still be in L2 when it is asked for (with the hint, 64-token pages
-  // went from 129 to 152 us on the Llama-3.1-8B decode batch).
-  static constexpr bool kStreamK = Stream;
+  // went from 129 to 152 us on the Llama-3.1-8B decode batch).  Key loads
+  // stream only with 64-token pages: with 16- and 32-token pages the hint on
+  // the values alone is faster (Llama-3.1-8B decode step 114.6-114.9 ->
+  // 109.8-110.5 us, its attention call 110.5-111.0 -> 107.5-107.7 us, the
+  // Llama-2-7B sweep expanded to 32 kv heads 191.3-191.4 -> 182.1-182.7 us;
+  // 64-token pages 125.2-125.6 -> 128.4-128.9 us, so they keep it).
+  static constexpr bool kStreamK = Stream && BS * 2 > 64;
   static constexpr bool kStreamV = Stream && BS * 2 <= 64;
   static constexpr bool kPipelined = true;  // double-buffered tile loop
   static constexpr int KC = D / 32;   // 16-byte chunks per lane per Q.K^T product
