@@ -43,7 +43,7 @@ METRIC = "paged GQA decode effective KV GB/s (% HBM peak); mixed-batch tokens/s"
 # `bench.py --copy-calibration`.  Valid only for the decode sources it was
 # measured on (their SHA-256 below); otherwise reported as null.
 DECODE_SOURCES = ["attention.hip", "decode_core.h", "gqa_common.h", "gqa_internal.h", "abi.hip"]
-DECODE_TRAFFIC = {"sources_sha256": "db31d98f43eb069af11d7b204c04ab4f56fb7885e3980a0a02eb83e3dd26dfab", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 669638452, "write_bytes_per_call": 8541824, "hbm_bytes_per_call": 678180276, "fetch_factor": 1.9999, "write_factor": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "8f59521f386ef659462c58c8f96826b7058c9cc0153742d94c275ab2f8089459", "partition_size": 0, "seed": 2, "fetch_bytes_per_call": 657209634, "write_bytes_per_call": 8565856, "hbm_bytes_per_call": 665775490, "fetch_factor": 1.9999, "write_factor": 1.0}
 
 
 def parse():
